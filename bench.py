@@ -1,0 +1,247 @@
+"""Benchmark: MoE expert-FFN tokens/s on one MI355X, with the roofline of the
+dominant kernel and the CPU oracle timed beside it.
+
+One step = the whole forward path over one batch: moe_dispatch (router top-k +
+softmax + stable COPY dispatch) -> awq_grouped_swiglu -> awq_grouped_down ->
+moe_combine.  Inputs are seeded synthetic tensors resident in HBM before the
+timed region.  Each step reads a different replica of the expert weights (as
+consecutive MoE layers would), so no step finds the previous step's weights in
+the 256 MB last-level cache.  Steps are captured once as HIP graphs and replayed.
+
+Prints ONE JSON line.  Default workload: the decode-shaped AWQ MoE
+(T=64, hidden 2048, intermediate 768, 128 experts, top_k 8, group 128, bf16).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+METRIC = "MoE expert-FFN tokens/s at 1 GPU; % of HBM (decode) / MFMA (prefill) peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="decode",
+                    choices=["tiny", "decode", "prefill", "many", "mxfp4"])
+    ap.add_argument("--replica-bytes", type=float, default=1.2e9,
+                    help="weight bytes cycled through by consecutive steps")
+    ap.add_argument("--eager", action="store_true", help="no HIP graph capture")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def workload_name(cfg):
+    kind = {"tiny": "tiny AWQ MoE FFN", "decode": "decode-shaped AWQ MoE FFN",
+            "prefill": "prefill-shaped AWQ MoE FFN", "many": "many-expert AWQ MoE FFN",
+            "mxfp4": "MXFP4 interleaved-bank MoE FFN"}[cfg.name]
+    return (f"{kind}: T={cfg.T} hidden={cfg.H} intermediate={cfg.I} E={cfg.E} "
+            f"top_k={cfg.k} group={cfg.group} act={cfg.adt} scales={cfg.sdt}")
+
+
+def alg_bytes(p, offsets):
+    """Algorithmic bytes of one step, from the actual routing.
+
+    Weights: packed words, zeros, scales and bias of touched experts only.
+    Activations: logits, x, values write+read, h write+read, y write+read,
+    weights, out."""
+    import numpy as np
+    E, T, k, H, I = p["E"], p["T"], p["k"], p["H"], p["I"]
+    A = T * k
+    counts = np.diff(offsets)
+    touched = int(np.count_nonzero(counts))
+    ab = 4 if p["adt"] == "f32" else 2
+    if p["fmt"] == "awq":
+        sb = {"f32": 4, "f16": 2, "bf16": 2}[p["sdt"]]
+        g = p["group"]
+
+        def cube(K, N, bias):
+            return K * N // 2 + (K // g) * (N // 8) * 4 + (K // g) * N * sb + (N * sb if bias else 0)
+        gu_e = 2 * cube(H, I, p["gate_b"] is not None)
+        dn_e = cube(I, H, p["down_b"] is not None)
+    else:
+        gu_e = 2 * I * (H // 32) * 17 + 2 * I * 2
+        dn_e = H * (I // 32) * 17 + H * 2
+    w_gu, w_dn = touched * gu_e, touched * dn_e
+    act_gu = A * H * ab + A * I * ab                 # values read, h written
+    act_dn = A * I * ab + A * H * ab                 # h read, y written
+    act_other = T * E * 4 + T * H * ab + A * H * ab + T * k * 4 + A * H * ab + T * H * ab
+    return dict(touched=touched, gateup=w_gu + act_gu, down=w_dn + act_dn,
+                total=w_gu + w_dn + act_gu + act_dn + act_other, weights=w_gu + w_dn)
+
+
+def flops(p):
+    A = p["T"] * p["k"]
+    return 6 * A * p["H"] * p["I"]
+
+
+def cpu_baseline(cfg, target_s):
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    from quantized_moe_expert_router_amd.synth import make_inputs
+    T = cfg.T if cfg.name in ("tiny", "decode") else min(cfg.T, 16)
+    p = make_inputs(cfg, T=T)
+    oracle._load()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.moe_forward(p, keep_intermediates=False)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 1000:
+            break
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    return {"value": round(reps * T / el, 3), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{reps} x full forward of a {T}-token batch of this workload "
+                      f"({el:.1f} s, double accumulation, OpenMP)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path "
+              "shards by tokens or by expert ranges, but this build runs on one GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quantized_moe_expert_router_amd import device_inputs as di
+    from quantized_moe_expert_router_amd import moeq
+    from quantized_moe_expert_router_amd.synth import CONFIGS, make_inputs, weight_bytes
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    moeq.lib()
+    p = make_inputs(cfg)
+    base = di.upload(p, dev)
+    wb = weight_bytes(p)
+    R = max(2, math.ceil(args.replica_bytes / wb))
+    wkeys = ("gate", "up_arg", "down")
+
+    def clone(w):
+        if w is None:
+            return None
+        if isinstance(w, moeq.AwqExperts):
+            return moeq.AwqExperts(w.qweight.clone(), w.qzeros.clone(), w.scales.clone(),
+                                   w.group_size, None if w.bias is None else w.bias.clone())
+        return moeq.Mxfp4Bank(w.blocks.clone(), w.scales.clone(), w.bias.clone(),
+                              w.interleaved_gate_up)
+    replicas = [{k: base[k] for k in wkeys}] + [{k: clone(base[k]) for k in wkeys}
+                                               for _ in range(R - 1)]
+
+    T, k, H, I, E = cfg.T, cfg.k, cfg.H, cfg.I, cfg.E
+    A = T * k
+    adt = base["x"].dtype
+    route = moeq.RouteState(T, E, k, dev)
+    bufs = dict(values=torch.empty(A, H, dtype=adt, device=dev),
+                weights=torch.empty(T, k, dtype=torch.float32, device=dev),
+                selected=torch.empty(T, k, dtype=torch.int32, device=dev),
+                row_experts=torch.empty(A, dtype=torch.int32, device=dev))
+    h = torch.empty(A, I, dtype=adt, device=dev)
+    y = torch.empty(A, H, dtype=adt, device=dev)
+    out = torch.empty(T, H, dtype=adt, device=dev)
+
+    def step(i):
+        w = replicas[i % R]
+        moeq.moe_dispatch(base["x"], base["logits"], base["router_bias"], k, route, bufs)
+        moeq.awq_grouped_swiglu(route, bufs["values"], w["gate"], w["up_arg"], cfg.clamp, 1.0,
+                                0.0, h)
+        moeq.awq_grouped_down(route, h, w["down"], y)
+        moeq.moe_combine(route, y, bufs["weights"], out)
+
+    # warm-up (also before capture, on a side stream as graph capture expects)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(max(args.warmup, R)):
+            step(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    graphs = None
+    if not args.eager:
+        graphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        if graphs is not None:
+            graphs[i % R].replay()
+        else:
+            step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- dominant kernel (gate/up projection): per-launch HIP events on its stream
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i, (a, b) in enumerate(evs):
+        w = replicas[i % R]
+        a.record(stream)
+        moeq.awq_grouped_swiglu(route, bufs["values"], w["gate"], w["up_arg"], cfg.clamp, 1.0,
+                                0.0, h)
+        b.record(stream)
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    offsets = route.expert_offsets.cpu().numpy()
+    ab = alg_bytes(p, offsets)
+    F = flops(p)
+    tok_s = T / (ms * 1e-3)
+    achieved = ab["gateup"] / (k_ms * 1e-3) / 1e9
+    path_gbs = ab["total"] / (ms * 1e-3) / 1e9
+    path_tflops = F / (ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.adt == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": workload_name(cfg), "tokens": T, "assignments": A,
+                   "touched_experts": ab["touched"], "weight_replicas": R,
+                   "graph": graphs is not None},
+        "roofline": {"kernel": "awq_grouped_swiglu (gate/up dequant-GEMM + SwiGLU)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel_ms": round(k_ms, 5),
+                     "alg_bytes_per_launch": ab["gateup"]},
+        "path": {"alg_bytes": ab["total"], "alg_flops": F, "GBs": round(path_gbs, 1),
+                 "hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
+                 "TFLOPs": round(path_tflops, 2),
+                 "mfma_frac": round(path_tflops / BF16_PEAK_TFLOPS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,230 @@
+/*
+ * moeq.h -- C-ABI of libmoeq.so: the routed mixture-of-experts expert FFN over
+ * frozen packed 4-bit expert weights, on one AMD Instinct MI355X (gfx950).
+ *
+ * The forward path is five calls on one stream:
+ *   moe_dispatch         router top-k + FP32 softmax weights + COPY dispatch
+ *   awq_grouped_swiglu   grouped gate/up projections dequantised in registers,
+ *                        storage-rounded SwiGLU
+ *   awq_grouped_down     grouped down projection
+ *   moe_combine          ascending expert-ID weighted combine back to tokens
+ * plus moe_dispatch_counts (range counts on the host) and awq_input_backward
+ * (input VJP through the same rounded coefficients).
+ *
+ * Sources (the pages the operations are defined on):
+ *   ruda-tensor 0.21.38 src/moe_exchange.rs    -- MoeDispatched, MoeDispatchOps
+ *   ruda-tensor 0.21.34 src/packed_experts.rs  -- AwqExpertOptions,
+ *       AwqExpertPayload, PackedExpertPayload, PackedExpertAutodiffError,
+ *       FrozenPackedExpertOps
+ *   ruda-tensor 0.21.33 src/frozen_awq.rs      -- FrozenAwqError, FrozenAwqOps
+ *   libmir-metal 0.3.0 src/engine/clamped_routed/experts/native.rs
+ *       -- ExpertLayout::Native, native_layout / companions / validate
+ *
+ * Conventions for every call:
+ *  - All tensor arguments are device pointers to contiguous row-major memory
+ *    owned by the caller.  The library allocates no device memory, frees
+ *    nothing, and does not synchronise, except moe_dispatch_counts, which
+ *    returns host values and therefore synchronises its stream.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All kernels of a
+ *    call are enqueued on it; the call returns once they are enqueued.
+ *  - Arguments are validated on the host before anything is enqueued.  On a
+ *    validation error the call returns a negative status, enqueues nothing and
+ *    leaves every output untouched; moeq_last_error() then names the check.
+ *  - A launch failure returns MOEQ_EDEVICE (the pages' Native(E) error).
+ *  - There is never a dense fallback or a requantisation (frozen_awq.rs,
+ *    FrozenAwqError::Native): a shape or dtype the kernels do not implement
+ *    returns MOEQ_EUNSUPPORTED.
+ *  - Calls on one stream are ordered; calls that share output buffers on
+ *    different streams race.
+ */
+#ifndef MOEQ_H
+#define MOEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOEQ_OK = 0,
+    MOEQ_EINVAL = -1,        /* NULL pointer, negative size, unbound route      */
+    MOEQ_ESHAPE = -2,        /* inconsistent or non-divisible shapes, overflow  */
+    MOEQ_EDTYPE = -3,        /* unknown or mismatched storage type              */
+    MOEQ_ERANGE = -4,        /* expert range / prefix outside the routed IDs   */
+    MOEQ_EWORKSPACE = -5,    /* route workspace too small or misaligned         */
+    MOEQ_EUNSUPPORTED = -6,  /* valid input the kernels do not implement        */
+    MOEQ_EDEVICE = -7        /* HIP launch or copy failure                      */
+} moeq_status;
+
+typedef enum { MOEQ_F32 = 0, MOEQ_F16 = 1, MOEQ_BF16 = 2 } moeq_dtype;
+
+/* Packed payload tag (packed_experts.rs PackedExpertPayload): AWQ I32 words,
+ * or an MXFP4 expert bank (native.rs ExpertLayout::Native). */
+typedef enum { MOEQ_FMT_AWQ = 0, MOEQ_FMT_MXFP4_BANK = 1 } moeq_format;
+
+/*
+ * Route state: the "private native row mappings" of moe_exchange.rs
+ * (MoeDispatchOps::MoeDispatchState), produced only by moe_dispatch and read by
+ * the grouped projections, the counts and the combine.  A host struct holding
+ * device pointers into one caller-owned workspace (moeq_route_bind).
+ */
+typedef struct moeq_route {
+    int32_t T, E, top_k;       /* routed shape; every consumer checks it        */
+    int32_t token_blocks;      /* internal: token blocks of the stable scatter  */
+    void *workspace;           /* device, caller-owned                           */
+    size_t workspace_bytes;
+    int32_t *expert_offsets;   /* [E+1] first sorted row of each expert; [E]=A  */
+    int32_t *row_src;          /* [A]   source token of sorted row p            */
+    int32_t *slot_pos;         /* [T*top_k] sorted row of assignment (t, j)     */
+    int32_t *block_base;       /* internal [token_blocks*E]                      */
+    uint32_t magic;            /* set by moeq_route_bind                         */
+} moeq_route;
+
+/* Bytes of device workspace a route of this shape needs (0 on invalid sizes). */
+size_t moeq_route_workspace_bytes(int32_t T, int32_t E, int32_t top_k);
+
+/* Lay a route out in `workspace` (device memory, >= the bytes above, 256-byte
+ * aligned).  Host only; enqueues nothing.  Errors: EINVAL (NULL, sizes < 0 or
+ * top_k outside [1, E]), EWORKSPACE (too small / misaligned). */
+moeq_status moeq_route_bind(moeq_route *route, void *workspace, size_t bytes,
+                            int32_t T, int32_t E, int32_t top_k);
+
+/*
+ * Expert cube descriptor: AwqExpertOptions + AwqExpertPayload
+ * (packed_experts.rs), or an MXFP4 bank (native.rs ExpertLayout::Native).
+ *
+ * AWQ:   qweight int32 [E, K, N/8] (eight 4-bit codes per word, AWQ nibble
+ *        order: nibble i holds column 0 2 4 6 1 3 5 7 [i] of its group of 8),
+ *        qzeros  int32 [E, K/g, N/8] (same order), scales [E, K/g, N] in
+ *        scale_dtype (F32/F16/BF16), bias [E, N] in scale_dtype or NULL.
+ *        coefficient(k, n) = (code - zero) * scale rounded once to scale_dtype
+ *        (frozen_awq.rs FrozenAwqOps doc comment).
+ *        K = in_features, N = out_features (N % 8 == 0), g = group_size
+ *        (K % g == 0; the kernels implement g % 32 == 0).
+ * MXFP4: qweight uint8 blocks [E, N, K/32, 16] (row = output feature, 32
+ *        E2M1 elements per 16 bytes, even element in the low nibble),
+ *        scales uint8 E8M0 [E, N, K/32], bias bf16 [E, N] (required, as the
+ *        bank layout has one), qzeros NULL, scale_dtype ignored,
+ *        group_size 32.  A gate/up bank has N = 2*I and interleaved_gate_up = 1
+ *        (row 2i = gate feature i, row 2i+1 = up feature i); a down bank has
+ *        interleaved_gate_up = 0 (native.rs native_layout / companions).
+ * experts / expert_start: the resident cubes cover global IDs
+ *        [expert_start, expert_start + experts); on one GPU this must be the
+ *        route's full range [0, E) (else ERANGE: no unchecked imported offsets).
+ */
+typedef struct moeq_experts {
+    moeq_format format;
+    int32_t experts;
+    int32_t expert_start;
+    int32_t in_features;
+    int32_t out_features;
+    int32_t group_size;
+    const void *qweight;
+    const void *qzeros;
+    const void *scales;
+    moeq_dtype scale_dtype;
+    const void *bias;
+    int32_t interleaved_gate_up;
+} moeq_experts;
+
+/* SwiGLU parameters: h = g' * sigmoid(alpha * g') * (u' + up_offset) with
+ * g', u' clamped to [-clamp, clamp] when clamp > 0.  Plain SwiGLU is
+ * {0, 1, 0}; the clamped routed variant of native.rs's engine is {7, 1, 0}. */
+typedef struct moeq_swiglu {
+    float clamp;
+    float alpha;
+    float up_offset;
+} moeq_swiglu;
+
+/*
+ * moe_dispatch -- moe_exchange.rs MoeDispatchOps::moe_dispatch / MoeDispatched.
+ *   x        [T, K] act (F32 or BF16)          input rows
+ *   logits   [T, E] fp32                        router logits
+ *   expert_bias [E] fp32 or NULL                added to the logits (one fp32
+ *                                               add) before selection and softmax
+ * Outputs (A = T * top_k):
+ *   values      [A, K] act   expert-sorted bit copies of the source rows
+ *   weights     [T, top_k] fp32  softmax over the selected scores
+ *   selected    [T, top_k] u32   expert IDs, descending score, ties -> lower ID
+ *   row_experts [A] u32      expert ID of each sorted row (non-decreasing)
+ *   route        bound to (T, E, top_k); receives the row mappings
+ * The sort is stable: the rows of one expert keep ascending token order.
+ * Implemented for E <= 2048, top_k <= 32 (else EUNSUPPORTED).  T = 0: no-op.
+ */
+moeq_status moe_dispatch(const void *x, moeq_dtype act, int32_t T, int32_t K,
+                         const float *logits, int32_t E, const float *expert_bias,
+                         int32_t top_k, void *values, float *weights,
+                         uint32_t *selected, uint32_t *row_experts,
+                         moeq_route *route, void *stream);
+
+/*
+ * moe_dispatch_counts -- moe_exchange.rs MoeDispatchOps::moe_dispatch_counts:
+ * rows per caller-declared contiguous range of global expert IDs, read from
+ * the expert offsets only.  expert_prefix: host int64 [R+1], non-decreasing,
+ * within [0, E] (else ERANGE); counts: host int64 [R],
+ * counts[r] = rows routed to experts [prefix[r], prefix[r+1]).
+ * Copies E+1 offsets to the host and synchronises `stream`.
+ */
+moeq_status moe_dispatch_counts(const moeq_route *route, const int64_t *expert_prefix,
+                                int32_t R, int64_t *counts, void *stream);
+
+/*
+ * awq_grouped_swiglu -- packed_experts.rs FrozenPackedExpertOps::
+ * packed_swiglu_forward, gate/up half: for the rows of each expert e,
+ *   G = values . Wg_e (+ bg_e), U = values . Wu_e (+ bu_e),
+ *   rounded to act, then h = round_act(SwiGLU(G, U)).
+ *   values [A, K] act (from moe_dispatch), h [A, I] act.
+ * AWQ: gate and up are two descriptors of equal shape [E, K, I/8].
+ * MXFP4: gate is an interleaved gate/up bank (N = 2I), up must be NULL.
+ * Only experts with rows are read (untouched experts cost no bytes).
+ */
+moeq_status awq_grouped_swiglu(const moeq_route *route, const void *values,
+                               moeq_dtype act, const moeq_experts *gate,
+                               const moeq_experts *up, moeq_swiglu fn, void *h,
+                               void *stream);
+
+/*
+ * awq_grouped_down -- the down projection of packed_swiglu_forward:
+ *   y = round_act(h . Wd_e (+ bd_e)),  h [A, I] act, y [A, K] act.
+ * AWQ down: [E, I, K/8] words; MXFP4: a non-interleaved bank [E, K, I/32, 16].
+ */
+moeq_status awq_grouped_down(const moeq_route *route, const void *h, moeq_dtype act,
+                             const moeq_experts *down, void *y, void *stream);
+
+/*
+ * moe_combine -- moe_exchange.rs MoeDispatchOps::moe_combine: ascending
+ * expert-ID combine after the rows returned to their source:
+ *   out[t, :] = round_act( fp32 sum, in ascending expert ID, of
+ *               weights[t, j] * y[slot_pos[t, j], :] )
+ * written as acc = fma(w, y, acc) from acc = 0.
+ *   y [A, K] act, weights [T, top_k] fp32, out [T, K] act.
+ */
+moeq_status moe_combine(const moeq_route *route, const void *y, moeq_dtype act,
+                        int32_t K, const float *weights, void *out, void *stream);
+
+/*
+ * awq_input_backward -- frozen_awq.rs FrozenAwqOps::frozen_awq_input_backward
+ * and packed_experts.rs packed_expert_input_backward: the transpose of the
+ * same rounded packed coefficients, no weight / scale / bias gradients:
+ *   grad_in[p, :] = round_gdt( grad[p, :] . W_e^T )
+ *   grad [rows, N] gdt, grad_in [rows, K] gdt (gdt F32 or BF16).
+ * route != NULL: rows must equal the route's A and row p uses the expert of
+ * sorted row p.  route == NULL: the single frozen projection; w must hold one
+ * expert and every row uses it.  AWQ only.
+ */
+moeq_status awq_input_backward(const moeq_route *route, const void *grad,
+                               moeq_dtype gdt, int32_t rows, const moeq_experts *w,
+                               void *grad_in, void *stream);
+
+/* Static text for a status code. */
+const char *moeq_status_string(moeq_status status);
+
+/* Text of the last validation or device error raised on the calling thread. */
+const char *moeq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOEQ_H */

@@ -1,0 +1,407 @@
+// api.cpp -- the C-ABI of libmoeq: host-side validation, then kernel launches.
+//
+// Every entry point checks its arguments completely before it enqueues
+// anything; a failed check returns a negative moeq_status, records the reason
+// for moeq_last_error() and leaves all outputs untouched.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "internal.hpp"
+#include "moeq.h"
+
+namespace moeq {
+hipError_t launch_fast_swiglu(const ProjProblem &p, hipStream_t s, bool *handled);
+hipError_t launch_fast_plain(const ProjProblem &p, hipStream_t s, bool *handled);
+}  // namespace moeq
+
+using namespace moeq;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+moeq_status fail(moeq_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+moeq_status device_status(hipError_t err, const char *what) {
+    if (err == hipSuccess) return MOEQ_OK;
+    return fail(MOEQ_EDEVICE, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool valid_dtype(int d) { return d == MOEQ_F32 || d == MOEQ_F16 || d == MOEQ_BF16; }
+size_t dtype_bytes(int d) { return d == MOEQ_F32 ? 4 : 2; }
+
+// a * b with overflow detection (native.rs validate: ShapeOverflow)
+bool mul_ok(size_t a, size_t b, size_t *out) {
+    if (a != 0 && b > SIZE_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Layout {
+    size_t off_offsets, off_row_src, off_slot_pos, off_block_base, total;
+    int blocks;
+};
+
+bool route_layout(int32_t T, int32_t E, int32_t k, Layout *L) {
+    if (T < 0 || E < 1 || k < 1 || k > E) return false;
+    size_t A;
+    if (!mul_ok((size_t)T, (size_t)k, &A) || A > (size_t)INT32_MAX) return false;
+    L->blocks = (int)((T + kTokenBlock - 1) / kTokenBlock);
+    size_t bb;
+    if (!mul_ok((size_t)L->blocks, (size_t)E, &bb)) return false;
+    size_t o = 0;
+    L->off_offsets = o;
+    o += align256(sizeof(int32_t) * ((size_t)E + 1));
+    L->off_row_src = o;
+    o += align256(sizeof(int32_t) * (A ? A : 1));
+    L->off_slot_pos = o;
+    o += align256(sizeof(int32_t) * (A ? A : 1));
+    L->off_block_base = o;
+    o += align256(sizeof(int32_t) * (bb ? bb : 1));
+    L->total = o;
+    return true;
+}
+
+moeq_status check_route(const moeq_route *r) {
+    if (!r) return fail(MOEQ_EINVAL, "route is NULL");
+    if (r->magic != kRouteMagic || !r->expert_offsets || !r->row_src || !r->slot_pos ||
+        !r->block_base)
+        return fail(MOEQ_EINVAL, "route was not bound by moeq_route_bind");
+    Layout L;
+    if (!route_layout(r->T, r->E, r->top_k, &L) || L.blocks != r->token_blocks)
+        return fail(MOEQ_EINVAL, "route shape (T=%d, E=%d, top_k=%d) is invalid", r->T, r->E,
+                    r->top_k);
+    return MOEQ_OK;
+}
+
+// Validate one expert cube against the route and the expected geometry.
+// want_K / want_N < 0: not constrained.
+moeq_status check_experts(const moeq_experts *w, const char *name, int route_E, int want_K,
+                          int want_N, bool want_interleaved) {
+    if (!w) return fail(MOEQ_EINVAL, "%s descriptor is NULL", name);
+    if (w->experts < 1 || w->in_features < 1 || w->out_features < 1 || w->group_size < 1 ||
+        w->expert_start < 0)
+        return fail(MOEQ_EINVAL, "%s: sizes must be positive", name);
+    if (route_E >= 0 && (w->expert_start != 0 || w->experts != route_E))
+        return fail(MOEQ_ERANGE,
+                    "%s: resident experts [%d, %d) must cover the routed IDs [0, %d)", name,
+                    w->expert_start, w->expert_start + w->experts, route_E);
+    if (want_K >= 0 && w->in_features != want_K)
+        return fail(MOEQ_ESHAPE, "%s: in_features %d, expected %d", name, w->in_features, want_K);
+    if (want_N >= 0 && w->out_features != want_N)
+        return fail(MOEQ_ESHAPE, "%s: out_features %d, expected %d", name, w->out_features,
+                    want_N);
+    if (!w->qweight || !w->scales) return fail(MOEQ_EINVAL, "%s: NULL payload pointer", name);
+    size_t n;
+    // coefficient count must be a size some device could hold (2^48 codes)
+    if (!mul_ok((size_t)w->experts, (size_t)w->in_features, &n) ||
+        !mul_ok(n, (size_t)w->out_features, &n) || n > ((size_t)1 << 48))
+        return fail(MOEQ_ESHAPE, "%s: size overflow", name);
+    if (w->format == MOEQ_FMT_AWQ) {
+        if (w->out_features % 8 != 0)
+            return fail(MOEQ_ESHAPE, "%s: out_features %d not divisible by 8", name,
+                        w->out_features);
+        if (w->in_features % w->group_size != 0)
+            return fail(MOEQ_ESHAPE, "%s: in_features %d not a whole number of groups of %d",
+                        name, w->in_features, w->group_size);
+        if (!w->qzeros) return fail(MOEQ_EINVAL, "%s: NULL qzeros", name);
+        if (!valid_dtype(w->scale_dtype))
+            return fail(MOEQ_EDTYPE, "%s: unknown scale dtype %d", name, (int)w->scale_dtype);
+        if (w->group_size % 32 != 0)
+            return fail(MOEQ_EUNSUPPORTED, "%s: group size %d (kernels take multiples of 32)",
+                        name, w->group_size);
+        if (w->interleaved_gate_up)
+            return fail(MOEQ_EUNSUPPORTED, "%s: interleaved gate/up applies to MXFP4 banks",
+                        name);
+    } else if (w->format == MOEQ_FMT_MXFP4_BANK) {
+        if (w->in_features % 32 != 0)
+            return fail(MOEQ_ESHAPE, "%s: in_features %d not a whole number of 32-blocks", name,
+                        w->in_features);
+        if (w->group_size != 32)
+            return fail(MOEQ_ESHAPE, "%s: MXFP4 block is 32, got group %d", name, w->group_size);
+        if (w->qzeros) return fail(MOEQ_EINVAL, "%s: MXFP4 bank has no zero words", name);
+        if (!w->bias) return fail(MOEQ_EINVAL, "%s: requires MXFP4 scales and BF16 bias", name);
+        if ((w->interleaved_gate_up != 0) != want_interleaved)
+            return fail(MOEQ_ESHAPE, want_interleaved
+                                         ? "%s: requires an interleaved gate/up expert bank"
+                                         : "%s: matrix-bank layout differs from routed role",
+                        name);
+    } else {
+        return fail(MOEQ_EDTYPE, "%s: unknown format %d", name, (int)w->format);
+    }
+    return MOEQ_OK;
+}
+
+PackedOperand operand_of(const moeq_experts *w) {
+    PackedOperand o;
+    o.format = w->format;
+    o.sdt = w->scale_dtype;
+    o.qw = static_cast<const int32_t *>(w->qweight);
+    o.qz = static_cast<const int32_t *>(w->qzeros);
+    o.scales = w->scales;
+    o.bias = w->bias;
+    o.K = w->in_features;
+    o.N = w->out_features;
+    o.g = w->group_size;
+    return o;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moeq_status_string(moeq_status s) {
+    switch (s) {
+    case MOEQ_OK: return "ok";
+    case MOEQ_EINVAL: return "invalid argument";
+    case MOEQ_ESHAPE: return "shape mismatch";
+    case MOEQ_EDTYPE: return "dtype mismatch";
+    case MOEQ_ERANGE: return "expert range";
+    case MOEQ_EWORKSPACE: return "workspace";
+    case MOEQ_EUNSUPPORTED: return "unsupported (no dense fallback)";
+    case MOEQ_EDEVICE: return "device error";
+    }
+    return "unknown status";
+}
+
+const char *moeq_last_error(void) { return g_last_error; }
+
+size_t moeq_route_workspace_bytes(int32_t T, int32_t E, int32_t top_k) {
+    Layout L;
+    return route_layout(T, E, top_k, &L) ? L.total : 0;
+}
+
+moeq_status moeq_route_bind(moeq_route *route, void *workspace, size_t bytes, int32_t T,
+                            int32_t E, int32_t top_k) {
+    if (!route || !workspace) return fail(MOEQ_EINVAL, "route or workspace is NULL");
+    Layout L;
+    if (!route_layout(T, E, top_k, &L))
+        return fail(MOEQ_EINVAL, "invalid route shape T=%d E=%d top_k=%d", T, E, top_k);
+    if ((uintptr_t)workspace % 256 != 0)
+        return fail(MOEQ_EWORKSPACE, "workspace must be 256-byte aligned");
+    if (bytes < L.total)
+        return fail(MOEQ_EWORKSPACE, "workspace has %zu bytes, needs %zu", bytes, L.total);
+    char *base = static_cast<char *>(workspace);
+    memset(route, 0, sizeof *route);
+    route->T = T;
+    route->E = E;
+    route->top_k = top_k;
+    route->token_blocks = L.blocks;
+    route->workspace = workspace;
+    route->workspace_bytes = bytes;
+    route->expert_offsets = reinterpret_cast<int32_t *>(base + L.off_offsets);
+    route->row_src = reinterpret_cast<int32_t *>(base + L.off_row_src);
+    route->slot_pos = reinterpret_cast<int32_t *>(base + L.off_slot_pos);
+    route->block_base = reinterpret_cast<int32_t *>(base + L.off_block_base);
+    route->magic = kRouteMagic;
+    return MOEQ_OK;
+}
+
+moeq_status moe_dispatch(const void *x, moeq_dtype act, int32_t T, int32_t K,
+                         const float *logits, int32_t E, const float *expert_bias,
+                         int32_t top_k, void *values, float *weights, uint32_t *selected,
+                         uint32_t *row_experts, moeq_route *route, void *stream) {
+    moeq_status st = check_route(route);
+    if (st != MOEQ_OK) return st;
+    if (route->T != T || route->E != E || route->top_k != top_k)
+        return fail(MOEQ_ESHAPE, "route bound for (T=%d, E=%d, top_k=%d), called with (%d, %d, %d)",
+                    route->T, route->E, route->top_k, T, E, top_k);
+    if (K < 1) return fail(MOEQ_EINVAL, "K must be positive");
+    if (!valid_dtype(act)) return fail(MOEQ_EDTYPE, "unknown activation dtype %d", (int)act);
+    if (E > kMaxExperts || top_k > kMaxTopK)
+        return fail(MOEQ_EUNSUPPORTED, "router implements E <= %d and top_k <= %d", kMaxExperts,
+                    kMaxTopK);
+    size_t row_bytes;
+    if (!mul_ok((size_t)K, dtype_bytes(act), &row_bytes))
+        return fail(MOEQ_ESHAPE, "size overflow");
+    if (T == 0) return MOEQ_OK;
+    if (!x || !logits || !values || !weights || !selected || !row_experts)
+        return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = device_status(launch_router(logits, expert_bias, T, E, top_k, selected, weights, s),
+                            "router")) != MOEQ_OK)
+        return st;
+    if ((st = device_status(launch_dispatch_index(selected, T, E, top_k, route, row_experts, s),
+                            "dispatch index")) != MOEQ_OK)
+        return st;
+    return device_status(launch_copy_rows(x, row_bytes, T * top_k, route->row_src, values, s),
+                         "row copy");
+}
+
+moeq_status moe_dispatch_counts(const moeq_route *route, const int64_t *expert_prefix,
+                                int32_t R, int64_t *counts, void *stream) {
+    moeq_status st = check_route(route);
+    if (st != MOEQ_OK) return st;
+    if (R < 0 || !expert_prefix || (R > 0 && !counts))
+        return fail(MOEQ_EINVAL, "bad prefix arguments");
+    for (int32_t r = 0; r <= R; ++r) {
+        if (expert_prefix[r] < 0 || expert_prefix[r] > route->E)
+            return fail(MOEQ_ERANGE, "prefix[%d] = %lld outside [0, %d]", r,
+                        (long long)expert_prefix[r], route->E);
+        if (r > 0 && expert_prefix[r] < expert_prefix[r - 1])
+            return fail(MOEQ_ERANGE, "prefix is not non-decreasing at %d", r);
+    }
+    if (R == 0) return MOEQ_OK;
+    std::vector<int32_t> off((size_t)route->E + 1, 0);
+    if (route->T > 0) {
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        if ((st = device_status(hipMemcpyAsync(off.data(), route->expert_offsets,
+                                               sizeof(int32_t) * off.size(),
+                                               hipMemcpyDeviceToHost, s),
+                                "offset copy")) != MOEQ_OK)
+            return st;
+        if ((st = device_status(hipStreamSynchronize(s), "stream sync")) != MOEQ_OK) return st;
+    }
+    for (int32_t r = 0; r < R; ++r)
+        counts[r] = (int64_t)off[expert_prefix[r + 1]] - (int64_t)off[expert_prefix[r]];
+    return MOEQ_OK;
+}
+
+moeq_status awq_grouped_swiglu(const moeq_route *route, const void *values, moeq_dtype act,
+                               const moeq_experts *gate, const moeq_experts *up,
+                               moeq_swiglu fn, void *h, void *stream) {
+    moeq_status st = check_route(route);
+    if (st != MOEQ_OK) return st;
+    if (!valid_dtype(act)) return fail(MOEQ_EDTYPE, "unknown activation dtype %d", (int)act);
+    if (!gate) return fail(MOEQ_EINVAL, "gate descriptor is NULL");
+    const bool bank = gate->format == MOEQ_FMT_MXFP4_BANK;
+    if ((st = check_experts(gate, "gate", route->E, -1, -1, bank)) != MOEQ_OK) return st;
+    int I;
+    if (bank) {
+        if (up) return fail(MOEQ_EINVAL, "an interleaved gate/up bank takes no up descriptor");
+        if (gate->out_features % 2 != 0)
+            return fail(MOEQ_ESHAPE, "gate/up bank rows %d are not 2*I", gate->out_features);
+        I = gate->out_features / 2;
+    } else {
+        if ((st = check_experts(up, "up", route->E, gate->in_features, gate->out_features,
+                                false)) != MOEQ_OK)
+            return st;
+        if (up->format != MOEQ_FMT_AWQ)
+            return fail(MOEQ_EDTYPE, "gate and up must share one format");
+        if (up->scale_dtype != gate->scale_dtype || up->group_size != gate->group_size)
+            return fail(MOEQ_EDTYPE, "gate and up must share scale dtype and group size");
+        if ((up->bias == nullptr) != (gate->bias == nullptr))
+            return fail(MOEQ_EINVAL, "gate and up must both have or both lack a bias");
+        I = gate->out_features;
+    }
+    if (act == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 activations are not implemented");
+    if (!(fn.clamp >= 0.0f) || !(fn.alpha == fn.alpha) || !(fn.up_offset == fn.up_offset))
+        return fail(MOEQ_EINVAL, "bad SwiGLU parameters");
+    const int A = route->T * route->top_k;
+    if (A == 0) return MOEQ_OK;
+    if (!values || !h) return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    ProjProblem p{};
+    p.in = values;
+    p.out = h;
+    p.offsets = route->expert_offsets;
+    p.rows = A;
+    p.E = route->E;
+    p.act = act;
+    p.Kred = gate->in_features;
+    p.Nout = I;
+    p.w0 = operand_of(gate);
+    p.w1 = bank ? p.w0 : operand_of(up);
+    p.mode = bank ? PROJ_BANK_SWIGLU : PROJ_SWIGLU;
+    p.clamp = fn.clamp;
+    p.alpha = fn.alpha;
+    p.up_offset = fn.up_offset;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    bool handled = false;
+    hipError_t err = launch_fast_swiglu(p, s, &handled);
+    if (!handled) err = launch_proj_generic(p, s);
+    return device_status(err, "gate/up projection");
+}
+
+moeq_status awq_grouped_down(const moeq_route *route, const void *h, moeq_dtype act,
+                             const moeq_experts *down, void *y, void *stream) {
+    moeq_status st = check_route(route);
+    if (st != MOEQ_OK) return st;
+    if (!valid_dtype(act)) return fail(MOEQ_EDTYPE, "unknown activation dtype %d", (int)act);
+    if ((st = check_experts(down, "down", route->E, -1, -1, false)) != MOEQ_OK) return st;
+    if (act == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 activations are not implemented");
+    const int A = route->T * route->top_k;
+    if (A == 0) return MOEQ_OK;
+    if (!h || !y) return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    ProjProblem p{};
+    p.in = h;
+    p.out = y;
+    p.offsets = route->expert_offsets;
+    p.rows = A;
+    p.E = route->E;
+    p.act = act;
+    p.Kred = down->in_features;
+    p.Nout = down->out_features;
+    p.w0 = operand_of(down);
+    p.w1 = p.w0;
+    p.mode = PROJ_PLAIN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    bool handled = false;
+    hipError_t err = launch_fast_plain(p, s, &handled);
+    if (!handled) err = launch_proj_generic(p, s);
+    return device_status(err, "down projection");
+}
+
+moeq_status moe_combine(const moeq_route *route, const void *y, moeq_dtype act, int32_t K,
+                        const float *weights, void *out, void *stream) {
+    moeq_status st = check_route(route);
+    if (st != MOEQ_OK) return st;
+    if (!valid_dtype(act)) return fail(MOEQ_EDTYPE, "unknown activation dtype %d", (int)act);
+    if (K < 1) return fail(MOEQ_EINVAL, "K must be positive");
+    if (route->T == 0) return MOEQ_OK;
+    if (!y || !weights || !out) return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    return device_status(launch_combine(y, act, weights, route->slot_pos, route->T, route->top_k,
+                                        K, out, static_cast<hipStream_t>(stream)),
+                         "combine");
+}
+
+moeq_status awq_input_backward(const moeq_route *route, const void *grad, moeq_dtype gdt,
+                               int32_t rows, const moeq_experts *w, void *grad_in,
+                               void *stream) {
+    moeq_status st;
+    if (route) {
+        if ((st = check_route(route)) != MOEQ_OK) return st;
+        if (rows != route->T * route->top_k)
+            return fail(MOEQ_ESHAPE, "rows %d != routed rows %d", rows, route->T * route->top_k);
+        if ((st = check_experts(w, "weights", route->E, -1, -1, false)) != MOEQ_OK) return st;
+    } else {
+        if (rows < 0) return fail(MOEQ_EINVAL, "rows must be >= 0");
+        if ((st = check_experts(w, "weights", -1, -1, -1, false)) != MOEQ_OK) return st;
+        if (w->experts != 1)
+            return fail(MOEQ_ERANGE, "without a route the cube must hold one expert, has %d",
+                        w->experts);
+    }
+    if (w->format != MOEQ_FMT_AWQ)
+        return fail(MOEQ_EUNSUPPORTED, "input VJP is implemented for AWQ cubes");
+    if (!valid_dtype(gdt)) return fail(MOEQ_EDTYPE, "unknown gradient dtype %d", (int)gdt);
+    if (gdt == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 gradients are not implemented");
+    if (rows == 0) return MOEQ_OK;
+    if (!grad || !grad_in) return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    ProjProblem p{};
+    p.in = grad;
+    p.out = grad_in;
+    p.offsets = route ? route->expert_offsets : nullptr;
+    p.rows = rows;
+    p.E = route ? route->E : 1;
+    p.act = gdt;
+    p.Kred = w->out_features;
+    p.Nout = w->in_features;
+    p.w0 = operand_of(w);
+    p.w1 = p.w0;
+    p.mode = PROJ_INPUT_VJP;
+    return device_status(launch_proj_generic(p, static_cast<hipStream_t>(stream)),
+                         "input VJP");
+}
+
+}  // extern "C"

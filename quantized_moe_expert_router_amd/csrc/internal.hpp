@@ -1,0 +1,65 @@
+// internal.hpp -- launcher declarations shared by the host API and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moeq.h"
+
+namespace moeq {
+
+constexpr uint32_t kRouteMagic = 0x6d6f6571u;  // "moeq"
+constexpr int kTokenBlock = 256;              // tokens per block of the stable scatter
+constexpr int kMaxTopK = 32;
+constexpr int kMaxExperts = 2048;
+
+// One packed projection operand as the kernels see it (validated on the host).
+struct PackedOperand {
+    int format;          // moeq_format
+    int sdt;             // scale dtype (AWQ)
+    const int32_t *qw;   // AWQ words  | MXFP4 block bytes (as int32 for alignment)
+    const int32_t *qz;   // AWQ zeros  | NULL
+    const void *scales;  // AWQ scales | MXFP4 E8M0 bytes
+    const void *bias;    // nullable
+    int K;               // reduction length of the forward projection (in_features)
+    int N;               // out_features of the cube
+    int g;               // AWQ group
+};
+
+// Projection problem: rows of `in` grouped by expert through `offsets`
+// (offsets == NULL: `rows` rows, all expert 0).
+struct ProjProblem {
+    const void *in;
+    void *out;
+    const int32_t *offsets;
+    int rows;            // total rows (A)
+    int E;               // experts in the grid
+    int act;             // activation / gradient storage
+    int Kred;            // reduction length
+    int Nout;            // output columns
+    PackedOperand w0;    // gate (or the only operand)
+    PackedOperand w1;    // up (AWQ gate/up only)
+    int mode;            // see ProjMode
+    float clamp, alpha, up_offset;
+};
+
+enum ProjMode {
+    PROJ_PLAIN = 0,      // out = in . W (+ b)
+    PROJ_SWIGLU = 1,     // out = SwiGLU(in . Wg (+ bg), in . Wu (+ bu)), AWQ
+    PROJ_BANK_SWIGLU = 2,// MXFP4 interleaved gate/up bank + SwiGLU
+    PROJ_INPUT_VJP = 3,  // out = in . W^T, AWQ (no bias)
+};
+
+hipError_t launch_router(const float *logits, const float *bias, int T, int E, int k,
+                         uint32_t *selected, float *weights, hipStream_t s);
+hipError_t launch_dispatch_index(const uint32_t *selected, int T, int E, int k,
+                                 const moeq_route *route, uint32_t *row_experts,
+                                 hipStream_t s);
+hipError_t launch_copy_rows(const void *x, size_t row_bytes, int A, const int32_t *row_src,
+                            void *values, hipStream_t s);
+hipError_t launch_combine(const void *y, int act, const float *weights,
+                          const int32_t *slot_pos, int T, int k, int K, void *out,
+                          hipStream_t s);
+hipError_t launch_proj_generic(const ProjProblem &p, hipStream_t s);
+
+}  // namespace moeq

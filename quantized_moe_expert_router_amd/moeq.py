@@ -1,0 +1,280 @@
+"""Thin Python binding of libmoeq.so (include/moeq.h): argument marshalling only.
+
+Every step of the path runs in the HIP library.  torch supplies device memory and
+the current stream; this module turns tensors into pointers, allocates outputs
+with torch, and raises :class:`MoeqError` on a negative status.  If the library
+is not built the first call raises; there is no other path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import dataclasses
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "csrc", "libmoeq.so")
+
+OK, EINVAL, ESHAPE, EDTYPE, ERANGE, EWORKSPACE, EUNSUPPORTED, EDEVICE = 0, -1, -2, -3, -4, -5, -6, -7
+F32, F16, BF16 = 0, 1, 2
+FMT_AWQ, FMT_MXFP4_BANK = 0, 1
+
+_TORCH_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+_DT_TORCH = {v: k for k, v in _TORCH_DT.items()}
+
+# every symbol include/moeq.h declares
+EXPORTS = ("moeq_route_workspace_bytes", "moeq_route_bind", "moe_dispatch",
+           "moe_dispatch_counts", "awq_grouped_swiglu", "awq_grouped_down", "moe_combine",
+           "awq_input_backward", "moeq_status_string", "moeq_last_error")
+
+
+class MoeqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"moeq status {status}: {message}")
+        self.status = status
+
+
+class Route(C.Structure):
+    """moeq_route: host struct of device pointers into one caller-owned workspace."""
+    _fields_ = [("T", C.c_int32), ("E", C.c_int32), ("top_k", C.c_int32),
+                ("token_blocks", C.c_int32), ("workspace", C.c_void_p),
+                ("workspace_bytes", C.c_size_t), ("expert_offsets", C.c_void_p),
+                ("row_src", C.c_void_p), ("slot_pos", C.c_void_p), ("block_base", C.c_void_p),
+                ("magic", C.c_uint32)]
+
+
+class Experts(C.Structure):
+    """moeq_experts: one packed expert cube (AWQ or MXFP4 bank)."""
+    _fields_ = [("format", C.c_int), ("experts", C.c_int32), ("expert_start", C.c_int32),
+                ("in_features", C.c_int32), ("out_features", C.c_int32),
+                ("group_size", C.c_int32), ("qweight", C.c_void_p), ("qzeros", C.c_void_p),
+                ("scales", C.c_void_p), ("scale_dtype", C.c_int), ("bias", C.c_void_p),
+                ("interleaved_gate_up", C.c_int32)]
+
+
+class SwiGLU(C.Structure):
+    _fields_ = [("clamp", C.c_float), ("alpha", C.c_float), ("up_offset", C.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoeq.so once; raise if it is missing (there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                           "(there is no CPU or PyTorch fallback)")
+    L = C.CDLL(LIB_PATH)
+    vp, i32 = C.c_void_p, C.c_int32
+    L.moeq_route_workspace_bytes.restype = C.c_size_t
+    L.moeq_route_workspace_bytes.argtypes = [i32, i32, i32]
+    L.moeq_route_bind.restype = C.c_int
+    L.moeq_route_bind.argtypes = [C.POINTER(Route), vp, C.c_size_t, i32, i32, i32]
+    L.moe_dispatch.restype = C.c_int
+    L.moe_dispatch.argtypes = [vp, C.c_int, i32, i32, vp, i32, vp, i32, vp, vp, vp, vp,
+                               C.POINTER(Route), vp]
+    L.moe_dispatch_counts.restype = C.c_int
+    L.moe_dispatch_counts.argtypes = [C.POINTER(Route), vp, i32, vp, vp]
+    L.awq_grouped_swiglu.restype = C.c_int
+    L.awq_grouped_swiglu.argtypes = [C.POINTER(Route), vp, C.c_int, C.POINTER(Experts),
+                                     C.POINTER(Experts), SwiGLU, vp, vp]
+    L.awq_grouped_down.restype = C.c_int
+    L.awq_grouped_down.argtypes = [C.POINTER(Route), vp, C.c_int, C.POINTER(Experts), vp, vp]
+    L.moe_combine.restype = C.c_int
+    L.moe_combine.argtypes = [C.POINTER(Route), vp, C.c_int, i32, vp, vp, vp]
+    L.awq_input_backward.restype = C.c_int
+    L.awq_input_backward.argtypes = [C.POINTER(Route), vp, C.c_int, i32, C.POINTER(Experts),
+                                     vp, vp]
+    L.moeq_status_string.restype = C.c_char_p
+    L.moeq_status_string.argtypes = [C.c_int]
+    L.moeq_last_error.restype = C.c_char_p
+    L.moeq_last_error.argtypes = []
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != OK:
+        L = lib()
+        raise MoeqError(status, f"{L.moeq_status_string(status).decode()}: "
+                                f"{L.moeq_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise MoeqError(EINVAL, "tensors must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> C.c_void_p:
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    return _TORCH_DT.get(t.dtype, 99)
+
+
+# ------------------------------------------------------------------ payloads
+@dataclasses.dataclass
+class AwqExperts:
+    """AWQ expert cube: qweight int32 [E,K,N/8], qzeros int32 [E,K/g,N/8],
+    scales [E,K/g,N] (fp32/fp16/bf16), bias [E,N] in the scale dtype or None."""
+    qweight: torch.Tensor
+    qzeros: torch.Tensor
+    scales: torch.Tensor
+    group_size: int
+    bias: Optional[torch.Tensor] = None
+    expert_start: int = 0
+
+    def c(self) -> Experts:
+        E, K, W8 = self.qweight.shape
+        return Experts(FMT_AWQ, E, self.expert_start, K, W8 * 8, self.group_size,
+                       _ptr(self.qweight), _ptr(self.qzeros), _ptr(self.scales),
+                       _dt(self.scales), _ptr(self.bias), 0)
+
+
+@dataclasses.dataclass
+class Mxfp4Bank:
+    """MXFP4 bank: blocks uint8 [E,R,C/32,16], scales uint8 [E,R,C/32], bias bf16 [E,R]."""
+    blocks: torch.Tensor
+    scales: torch.Tensor
+    bias: torch.Tensor
+    interleaved_gate_up: bool
+    expert_start: int = 0
+
+    def c(self) -> Experts:
+        E, R, NB, _ = self.blocks.shape
+        return Experts(FMT_MXFP4_BANK, E, self.expert_start, NB * 32, R, 32, _ptr(self.blocks),
+                       None, _ptr(self.scales), BF16, _ptr(self.bias),
+                       1 if self.interleaved_gate_up else 0)
+
+
+# ------------------------------------------------------------------ route
+class RouteState:
+    """A moeq_route plus the torch-owned workspace it points into."""
+
+    def __init__(self, T: int, E: int, top_k: int, device="cuda"):
+        nbytes = lib().moeq_route_workspace_bytes(T, E, top_k)
+        if nbytes == 0:
+            raise MoeqError(EINVAL, f"invalid route shape T={T} E={E} top_k={top_k}")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.c = Route()
+        _check(lib().moeq_route_bind(C.byref(self.c), _ptr(self.workspace), nbytes, T, E, top_k))
+        self.T, self.E, self.top_k = T, E, top_k
+        self.device = self.workspace.device
+
+    @property
+    def A(self) -> int:
+        return self.T * self.top_k
+
+    def _view(self, ptr_attr: str, n: int) -> torch.Tensor:
+        off = getattr(self.c, ptr_attr) - self.workspace.data_ptr()
+        return self.workspace[off:off + 4 * n].view(torch.int32)
+
+    @property
+    def expert_offsets(self) -> torch.Tensor:
+        return self._view("expert_offsets", self.E + 1)
+
+    @property
+    def row_src(self) -> torch.Tensor:
+        return self._view("row_src", self.A)
+
+    @property
+    def slot_pos(self) -> torch.Tensor:
+        return self._view("slot_pos", self.A).view(self.T, self.top_k)
+
+
+# ------------------------------------------------------------------ calls
+def moe_dispatch(x: torch.Tensor, logits: torch.Tensor, expert_bias: Optional[torch.Tensor],
+                 top_k: int, route: Optional[RouteState] = None, out: Optional[dict] = None):
+    """Router top-k + FP32 softmax + COPY dispatch.  Returns a dict with values,
+    weights, selected, row_experts and route (moe_exchange.rs MoeDispatched)."""
+    T, K = x.shape
+    E = logits.shape[1]
+    if route is None:
+        route = RouteState(T, E, top_k, x.device)
+    A = T * top_k
+    if out is None:
+        out = dict(values=torch.empty(A, K, dtype=x.dtype, device=x.device),
+                   weights=torch.empty(T, top_k, dtype=torch.float32, device=x.device),
+                   selected=torch.empty(T, top_k, dtype=torch.int32, device=x.device),
+                   row_experts=torch.empty(A, dtype=torch.int32, device=x.device))
+    if logits.dtype != torch.float32 or (expert_bias is not None and expert_bias.dtype != torch.float32):
+        raise MoeqError(EDTYPE, "logits and expert bias are fp32")
+    _check(lib().moe_dispatch(_ptr(x), _dt(x), T, K, _ptr(logits), E, _ptr(expert_bias), top_k,
+                              _ptr(out["values"]), _ptr(out["weights"]), _ptr(out["selected"]),
+                              _ptr(out["row_experts"]), C.byref(route.c), _stream(x.device)))
+    out["route"] = route
+    return out
+
+
+def moe_dispatch_counts(route: RouteState, expert_prefix: Sequence[int]) -> list:
+    """Rows per contiguous global expert range [prefix[r], prefix[r+1]) (synchronises)."""
+    pre = (C.c_int64 * len(expert_prefix))(*[int(v) for v in expert_prefix])
+    R = len(expert_prefix) - 1
+    cnt = (C.c_int64 * max(R, 1))()
+    _check(lib().moe_dispatch_counts(C.byref(route.c), C.cast(pre, C.c_void_p), R,
+                                     C.cast(cnt, C.c_void_p), _stream(route.device)))
+    return [int(cnt[i]) for i in range(max(R, 0))]
+
+
+def awq_grouped_swiglu(route: RouteState, values: torch.Tensor, gate, up=None,
+                       clamp: float = 0.0, alpha: float = 1.0, up_offset: float = 0.0,
+                       h: Optional[torch.Tensor] = None) -> torch.Tensor:
+    gc = gate.c()
+    uc = None if up is None else up.c()
+    I = gc.out_features // 2 if isinstance(gate, Mxfp4Bank) else gc.out_features
+    if h is None:
+        h = torch.empty(values.shape[0], I, dtype=values.dtype, device=values.device)
+    _check(lib().awq_grouped_swiglu(C.byref(route.c), _ptr(values), _dt(values), C.byref(gc),
+                                    None if uc is None else C.byref(uc),
+                                    SwiGLU(clamp, alpha, up_offset), _ptr(h),
+                                    _stream(values.device)))
+    return h
+
+
+def awq_grouped_down(route: RouteState, h: torch.Tensor, down,
+                     y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    dc = down.c()
+    if y is None:
+        y = torch.empty(h.shape[0], dc.out_features, dtype=h.dtype, device=h.device)
+    _check(lib().awq_grouped_down(C.byref(route.c), _ptr(h), _dt(h), C.byref(dc), _ptr(y),
+                                  _stream(h.device)))
+    return y
+
+
+def moe_combine(route: RouteState, y: torch.Tensor, weights: torch.Tensor,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    K = y.shape[1]
+    if out is None:
+        out = torch.empty(route.T, K, dtype=y.dtype, device=y.device)
+    _check(lib().moe_combine(C.byref(route.c), _ptr(y), _dt(y), K, _ptr(weights), _ptr(out),
+                             _stream(y.device)))
+    return out
+
+
+def awq_input_backward(route: Optional[RouteState], grad: torch.Tensor, w: AwqExperts,
+                       grad_in: Optional[torch.Tensor] = None) -> torch.Tensor:
+    wc = w.c()
+    rows = grad.shape[0]
+    if grad_in is None:
+        grad_in = torch.empty(rows, wc.in_features, dtype=grad.dtype, device=grad.device)
+    _check(lib().awq_input_backward(None if route is None else C.byref(route.c), _ptr(grad),
+                                    _dt(grad), rows, C.byref(wc), _ptr(grad_in),
+                                    _stream(grad.device)))
+    return grad_in
+
+
+def moe_ffn(x, logits, expert_bias, top_k, gate, up, down, clamp=0.0, alpha=1.0, up_offset=0.0):
+    """The whole forward path: dispatch -> gate/up + SwiGLU -> down -> combine."""
+    d = moe_dispatch(x, logits, expert_bias, top_k)
+    h = awq_grouped_swiglu(d["route"], d["values"], gate, up, clamp, alpha, up_offset)
+    y = awq_grouped_down(d["route"], h, down)
+    return moe_combine(d["route"], y, d["weights"]), d

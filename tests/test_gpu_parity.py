@@ -1,0 +1,204 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle.
+
+Bars: routing indices, dispatch order, offsets and value copies bit-exact; the
+combine bit-exact on identical inputs; projections and the end-to-end output
+within max relative error 1e-4 (fp32 activations) / 2e-2 (bf16 activations),
+measured per token row as ||got - ref||_inf / ||ref||_inf.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, TOL, f64, row_rel_err, run_path
+from quantized_moe_expert_router_amd import device_inputs as di
+from quantized_moe_expert_router_amd import moeq
+from quantized_moe_expert_router_amd.synth import CONFIGS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+ALL = ["tiny", "decode", "prefill", "many", "mxfp4"]
+# token counts the oracle evaluates whole in seconds, spanning several tiles
+SMALL_T = {"tiny": 16, "decode": 64, "prefill": 96, "many": 80, "mxfp4": 24}
+
+
+def check_dispatch(p, g):
+    sel, w = oracle.route(p["logits"], p["router_bias"], p["k"])
+    off, src, pos, rex = oracle.dispatch_index(sel, p["E"])
+    np.testing.assert_array_equal(g["selected"], sel)
+    np.testing.assert_array_equal(g["offsets"], off)
+    np.testing.assert_array_equal(g["row_src"], src)
+    np.testing.assert_array_equal(g["slot_pos"], pos)
+    np.testing.assert_array_equal(g["row_experts"], rex)
+    np.testing.assert_array_equal(g["values"], oracle.copy_rows(p["x"], src))
+    # FP32 softmax weights: both sides evaluate in double and round once to fp32
+    np.testing.assert_allclose(g["weights"], w, rtol=2.0 ** -23, atol=0)
+    return sel, w, off, src, pos, rex
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_dispatch_bit_exact_full_size(name):
+    p = make_inputs(CONFIGS[name])
+    print(f"[dispatch] {name} T={p['T']} E={p['E']} k={p['k']}", flush=True)
+    d = di.upload(p, DEV)
+    disp = moeq.moe_dispatch(d["x"], d["logits"], d["router_bias"], p["k"])
+    torch.cuda.synchronize()
+    r = disp["route"]
+    g = dict(selected=disp["selected"].cpu().numpy().view(np.uint32),
+             weights=disp["weights"].cpu().numpy(),
+             row_experts=disp["row_experts"].cpu().numpy().view(np.uint32),
+             values=di.to_host(disp["values"], p["adt"]), offsets=r.expert_offsets.cpu().numpy(),
+             row_src=r.row_src.cpu().numpy(), slot_pos=r.slot_pos.cpu().numpy())
+    check_dispatch(p, g)
+    off = g["offsets"]
+    prefix = [0, p["E"] // 4, p["E"] // 2, p["E"]]
+    assert moeq.moe_dispatch_counts(r, prefix) == oracle.counts(off, prefix).tolist()
+    assert sum(moeq.moe_dispatch_counts(r, [0, p["E"]])) == p["T"] * p["k"]
+
+
+@pytest.mark.parametrize("T,E,k", [(300, 128, 8), (77, 16, 4), (64, 512, 10), (5, 32, 32)])
+def test_router_ties_go_to_lower_id(T, E, k):
+    rng = np.random.default_rng(T + E + k)
+    logits = rng.integers(-2, 3, size=(T, E)).astype(np.float32)     # many exact ties
+    logits[0] = 0.0                                                  # one all-tie token
+    x = rng.normal(0, 1, (T, 64)).astype(np.float32)
+    disp = moeq.moe_dispatch(torch.from_numpy(x).to(DEV), torch.from_numpy(logits).to(DEV),
+                             None, k)
+    torch.cuda.synchronize()
+    sel, w = oracle.route(logits, None, k)
+    np.testing.assert_array_equal(disp["selected"].cpu().numpy().view(np.uint32), sel)
+    assert disp["selected"][0].cpu().tolist() == list(range(k))
+    np.testing.assert_allclose(disp["weights"].cpu().numpy(), w, rtol=2.0 ** -23, atol=0)
+    off, src, pos, rex = oracle.dispatch_index(sel, E)
+    np.testing.assert_array_equal(disp["route"].slot_pos.cpu().numpy(), pos)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_path_parity_small(name):
+    """Whole path at the config's shapes with a token count the oracle finishes
+    in seconds; every stage compared (each on identical inputs)."""
+    cfg = CONFIGS[name]
+    p = make_inputs(cfg, T=SMALL_T[name])
+    print(f"[path] {name} T={p['T']} H={p['H']} I={p['I']} E={p['E']} k={p['k']}", flush=True)
+    g = run_path(p)
+    sel, w, off, src, pos, rex = check_dispatch(p, g)
+    ref = oracle.moe_forward(p)
+    tol = TOL[p["adt"]]
+    assert row_rel_err(f64(g["h"], p["adt"]), f64(ref["h"], p["adt"])) <= tol
+    # down projection on the oracle's h (identical input)
+    h_or = di.tensor(ref["h"], p["adt"], DEV)
+    y_gpu = moeq.awq_grouped_down(g["route"], h_or, g["dev"]["down"])
+    y_gpu = di.to_host(y_gpu, p["adt"])
+    assert row_rel_err(f64(y_gpu, p["adt"]), f64(ref["y"], p["adt"])) <= tol
+    assert row_rel_err(f64(g["out"], p["adt"]), f64(ref["out"], p["adt"])) <= tol
+    # combine bit-exact on identical y and weights
+    y_or = di.tensor(ref["y"], p["adt"], DEV)
+    out_c = moeq.moe_combine(g["route"], y_or, g["disp"]["weights"])
+    out_ref = oracle.combine(ref["y"], p["adt"], g["weights"], pos)
+    np.testing.assert_array_equal(di.to_host(out_c, p["adt"]), out_ref)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_path_parity_full_size_sampled(name):
+    """Full workload in the bench's launch configuration; the oracle recomputes a
+    sample of tokens one by one (a token's output depends only on its own row)."""
+    p = make_inputs(CONFIGS[name])
+    print(f"[full] {name} T={p['T']}", flush=True)
+    g = run_path(p)
+    rng = np.random.default_rng(99)
+    n = min(p["T"], 24 if name in ("prefill", "mxfp4") else 48)
+    sample = np.sort(rng.choice(p["T"], size=n, replace=False))
+    sub = dict(p)
+    sub["T"] = n
+    sub["x"] = p["x"][sample]
+    sub["logits"] = p["logits"][sample]
+    ref = oracle.moe_forward(sub, keep_intermediates=False)
+    err = row_rel_err(f64(g["out"][sample], p["adt"]), f64(ref["out"], p["adt"]))
+    print(f"[full] {name} sampled rel err {err:.3e}", flush=True)
+    assert err <= TOL[p["adt"]]
+
+
+def test_run_to_run_bit_identical():
+    p = make_inputs(CONFIGS["decode"])
+    d = di.upload(p, DEV)
+    a, b = run_path(p, d), run_path(p, d)
+    for key in ("selected", "weights", "values", "h", "y", "out"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_edge_cases():
+    base = CONFIGS["decode"]
+    # one token, k = 1; untouched experts; E not a multiple of 64
+    for T, k, E in [(1, 1, 128), (3, 8, 100), (9, 2, 512)]:
+        cfg = dataclasses.replace(base, T=T, k=k, E=E, H=256, I=128)
+        p = make_inputs(cfg, seed=5)
+        g = run_path(p)
+        check_dispatch(p, g)
+        ref = oracle.moe_forward(p)
+        assert row_rel_err(f64(g["out"], "bf16"), f64(ref["out"], "bf16")) <= TOL["bf16"]
+    # T = 0 is a no-op through every call
+    d = di.upload(make_inputs(dataclasses.replace(base, H=256, I=128), seed=6), DEV)
+    x0 = torch.empty(0, 256, dtype=torch.bfloat16, device=DEV)
+    disp = moeq.moe_dispatch(x0, torch.empty(0, 128, device=DEV), None, 8)
+    h = moeq.awq_grouped_swiglu(disp["route"], disp["values"], d["gate"], d["up"])
+    y = moeq.awq_grouped_down(disp["route"], h, d["down"])
+    out = moeq.moe_combine(disp["route"], y, disp["weights"])
+    torch.cuda.synchronize()
+    assert out.shape == (0, 256)
+    assert moeq.moe_dispatch_counts(disp["route"], [0, 64, 128]) == [0, 0]
+
+
+@pytest.mark.parametrize("sdt,gdt", [("bf16", "bf16"), ("f16", "f32"), ("f32", "bf16")])
+def test_input_backward(sdt, gdt):
+    cfg = dataclasses.replace(CONFIGS["decode"], T=24, sdt=sdt, H=512, I=256)
+    p = make_inputs(cfg, seed=7)
+    d = di.upload(p, DEV)
+    disp = moeq.moe_dispatch(d["x"], d["logits"], None, p["k"])
+    r = disp["route"]
+    rng = np.random.default_rng(8)
+    A, N = p["T"] * p["k"], p["I"]
+    from quantized_moe_expert_router_amd.synth import to_storage
+    grad = to_storage(rng.normal(0, 1, (A, N)), gdt)
+    gi = moeq.awq_input_backward(r, di.tensor(grad, gdt, DEV), d["gate"])
+    torch.cuda.synchronize()
+    rex = disp["row_experts"].cpu().numpy().view(np.uint32)
+    ref = oracle.awq_input_backward(grad, gdt, rex, p["gate_qw"], p["gate_qz"], p["gate_s"], sdt,
+                                    p["group"])
+    tol = TOL[gdt]
+    assert row_rel_err(f64(di.to_host(gi, gdt), gdt), f64(ref, gdt)) <= tol
+    # single frozen projection: no route, one expert
+    one = moeq.AwqExperts(d["gate"].qweight[:1].contiguous(), d["gate"].qzeros[:1].contiguous(),
+                          d["gate"].scales[:1].contiguous(), p["group"])
+    g1 = moeq.awq_input_backward(None, di.tensor(grad[:40], gdt, DEV), one)
+    torch.cuda.synchronize()
+    ref1 = oracle.awq_input_backward(grad[:40], gdt, None, p["gate_qw"][:1], p["gate_qz"][:1],
+                                     p["gate_s"][:1], sdt, p["group"])
+    assert row_rel_err(f64(di.to_host(g1, gdt), gdt), f64(ref1, gdt)) <= tol
+
+
+def test_exact_arithmetic_projection_bit_exact():
+    """Power-of-two scales and small-integer activations: every product and partial
+    sum is exact, so GPU and oracle agree bit for bit whatever the summation order.
+    Pins indexing, grouping and the nibble permutation of the HIP kernels."""
+    cfg = dataclasses.replace(CONFIGS["decode"], T=40, H=512, I=256, E=16, k=4)
+    p = make_inputs(cfg, seed=9)
+    rng = np.random.default_rng(10)
+    for nm in ("gate", "up", "down"):
+        s = (2.0 ** -rng.integers(6, 9, size=p[nm + "_s"].shape)).astype(np.float32)
+        from quantized_moe_expert_router_amd.synth import to_storage
+        p[nm + "_s"] = to_storage(s.astype(np.float64), "bf16")
+    p["x"] = to_storage(rng.integers(-2, 3, size=p["x"].shape).astype(np.float64), "bf16")
+    g = run_path(p)
+    sel, w, off, src, pos, rex = check_dispatch(p, g)
+    # G and U are exact, so both sides round the same values to bf16; h then
+    # differs at most by the last-bit rounding of SwiGLU (fp32 exp vs double)
+    ref = oracle.moe_forward(p)
+    hg, hr = f64(g["h"], "bf16"), f64(ref["h"], "bf16")
+    assert np.all(np.abs(hg - hr) <= 2.0 ** -8 * np.abs(hr) + 1e-30)
+    hq = to_storage(rng.integers(-2, 3, size=(p["T"] * p["k"], p["I"])).astype(np.float64), "bf16")
+    y = moeq.awq_grouped_down(g["route"], di.tensor(hq, "bf16", DEV), g["dev"]["down"])
+    ref = oracle.awq_project(hq, "bf16", rex, p["down_qw"], p["down_qz"], p["down_s"], "bf16",
+                             p["group"])
+    np.testing.assert_array_equal(di.to_host(y, "bf16"), ref)
