@@ -202,3 +202,22 @@ def test_exact_arithmetic_projection_bit_exact():
     ref = oracle.awq_project(hq, "bf16", rex, p["down_qw"], p["down_qz"], p["down_s"], "bf16",
                              p["group"])
     np.testing.assert_array_equal(di.to_host(y, "bf16"), ref)
+
+
+@pytest.mark.parametrize("sdt,bias", [("bf16", False), ("f16", True), ("f32", True)])
+def test_skewed_routing_heavy_experts(sdt, bias):
+    """A strong router bias sends every token to experts 0..3: those experts get
+    T rows each (several 16-row passes) while most experts stay untouched."""
+    cfg = dataclasses.replace(CONFIGS["decode"], T=72, H=512, I=256, sdt=sdt, awq_bias=bias)
+    p = make_inputs(cfg, seed=11)
+    rb = np.zeros(p["E"], np.float32)
+    rb[:4] = 50.0
+    p["router_bias"] = rb
+    print(f"[skew] sdt={sdt} bias={bias}", flush=True)
+    g = run_path(p)
+    check_dispatch(p, g)
+    assert np.all(np.diff(g["offsets"])[:4] == p["T"])
+    ref = oracle.moe_forward(p)
+    tol = TOL["bf16"]
+    assert row_rel_err(f64(g["h"], "bf16"), f64(ref["h"], "bf16")) <= tol
+    assert row_rel_err(f64(g["out"], "bf16"), f64(ref["out"], "bf16")) <= tol
