@@ -2,18 +2,22 @@
 //
 // The AWQ payload (packed_experts.rs AwqExpertPayload; frozen_awq.rs
 // FrozenAwqOps) packs eight 4-bit codes of eight consecutive output columns
-// into one I32 word; a row of the cube is K-major: word (k, j) holds columns
-// 8j..8j+7 of input feature k.  The MFMA B operand wants, per lane, eight
-// consecutive k of one column.  A lane that reads the eight words (k..k+7, j)
-// therefore holds, for each of the 8 nibble positions, one complete B operand
-// for the column that nibble position encodes.  One MFMA per nibble position
-// covers 16 word columns (the 16 lanes of a row) -- the output column order is
-// permuted only at the store.  No cross-lane shuffles are needed.
+// into one I32 word; a cube is K-major: word (k, j) holds columns 8j..8j+7 of
+// input feature k.  The MFMA B operand wants, per lane, eight consecutive k of
+// one column.  A lane that reads the eight words (k..k+7, j) therefore holds,
+// for each of the 8 nibble positions, one complete B operand for the column
+// that nibble position encodes.  One 16x16x32 MFMA per nibble position covers
+// 16 word columns (the 16 lanes of a row); output columns are permuted only at
+// the store, and no cross-lane shuffles are needed.
 //
 // Coefficient: (code - zero) * scale, rounded to the scale dtype (the pages'
-// definition), formed in fp32 as fma(code, s, -zero*s), exact for bf16/fp16
-// scales, then rounded to bf16 for the MFMA (a no-op for bf16 scales).
+// definition).  Codes become floats exactly through the fp8 E4M3 converter
+// (a byte b < 16 encodes b * 2^-9), then fma(code', s * 2^9, -zero * s) gives
+// the exact product for bf16/fp16 scales; the pack to bf16 rounds once.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -24,90 +28,55 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Slot sl of a decoded word: bytes 0..3 of (w & 0x0F0F0F0F) are nibbles
-// 0,2,4,6 and bytes 0..3 of ((w >> 4) & 0x0F0F0F0F) nibbles 1,3,5,7.  Under the
-// AWQ order (nibble i holds column [0 2 4 6 1 3 5 7][i]) slot sl holds column:
+// Slot sl of a word: bytes 0..3 of (w & 0x0F0F0F0F) are nibbles 0,2,4,6 and
+// bytes 0..3 of ((w >> 4) & 0x0F0F0F0F) nibbles 1,3,5,7.  Under the AWQ order
+// (nibble i holds column [0 2 4 6 1 3 5 7][i]) slot sl holds column:
 __device__ constexpr int kSlotCol[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 
-// AND the compiler cannot fold into later byte extractions, so that each byte
-// converts with one v_cvt_f32_ubyteN.
+// Byte b < 16 read as OCP fp8 E4M3 is b * 2^-9 (exponent-0 subnormals continue
+// linearly into exponent 1); scales are pre-multiplied by 2^9 to compensate.
+constexpr float kCodeUnit = 512.0f;
+
+// AND the compiler cannot fold into later byte extractions.
 __device__ __forceinline__ uint32_t and_opaque(uint32_t x, uint32_t m) {
     uint32_t r;
     asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(m));
     return r;
 }
 
-// The eight 4-bit codes of a word as floats, in slot order.
+// The eight 4-bit codes of a word, in slot order, as code * 2^-9.
 __device__ __forceinline__ void decode_codes(uint32_t w, float q[8]) {
     const uint32_t lo = and_opaque(w, 0x0F0F0F0Fu);
     const uint32_t hi = and_opaque(w >> 4, 0x0F0F0F0Fu);
-    q[0] = (float)(lo & 0xFFu);
-    q[1] = (float)((lo >> 8) & 0xFFu);
-    q[2] = (float)((lo >> 16) & 0xFFu);
-    q[3] = (float)(lo >> 24);
-    q[4] = (float)(hi & 0xFFu);
-    q[5] = (float)((hi >> 8) & 0xFFu);
-    q[6] = (float)((hi >> 16) & 0xFFu);
-    q[7] = (float)(hi >> 24);
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+    const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+    q[0] = a[0]; q[1] = a[1]; q[2] = b[0]; q[3] = b[1];
+    q[4] = c[0]; q[5] = c[1]; q[6] = d[0]; q[7] = d[1];
 }
 
 // Per-group dequant constants of one word column, in slot order.
 template <int SD>
 struct GroupConst {
-    float s[8];   // scale
-    float zs[8];  // -zero * scale (16-bit scales) | zero (fp32 scales)
+    float s[8];   // scale * 2^9
+    float zs[8];  // -zero * scale (16-bit scales) | zero * 2^-9 (fp32 scales)
 };
 
-template <int SD>
-__device__ __forceinline__ void load_group(const uint32_t *qz, const void *scales, size_t zidx,
-                                           size_t sidx, GroupConst<SD> &gc) {
-    const uint32_t zw = qz[zidx];
-    float z[8];
-    decode_codes(zw, z);
-    float sv[8];
-    if (SD == MOEQ_F32) {
-        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(scales) + sidx);
-        const float4 v0 = p[0], v1 = p[1];
-        sv[0] = v0.x; sv[1] = v0.y; sv[2] = v0.z; sv[3] = v0.w;
-        sv[4] = v1.x; sv[5] = v1.y; sv[6] = v1.z; sv[7] = v1.w;
-    } else {
-        typedef typename Storage<SD>::T S;
-        typedef S s8 __attribute__((ext_vector_type(8)));
-        const s8 v = *reinterpret_cast<const s8 *>(static_cast<const S *>(scales) + sidx);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) sv[c] = (float)v[c];
-    }
-#pragma unroll
-    for (int sl = 0; sl < 8; ++sl) {
-        gc.s[sl] = sv[kSlotCol[sl]];
-        gc.zs[sl] = SD == MOEQ_F32 ? z[sl] : -z[sl] * gc.s[sl];  // exact: 4-bit x 16-bit
-    }
-}
-
-// Coefficient of slot sl from code q: the scale-dtype value, as fp32.
+// Coefficient of slot sl from q = code * 2^-9, as the scale-dtype value in fp32.
 template <int SD>
 __device__ __forceinline__ float coeff(float q, const GroupConst<SD> &gc, int sl) {
-    if (SD == MOEQ_F32) return (q - gc.zs[sl]) * gc.s[sl];        // RNE32((q-z)s)
-    const float v = __builtin_fmaf(q, gc.s[sl], gc.zs[sl]);         // exact (q-z)s
+    if (SD == MOEQ_F32) return (q - gc.zs[sl]) * gc.s[sl];        // RNE32((code-zero)s)
+    const float v = __builtin_fmaf(q, gc.s[sl], gc.zs[sl]);         // exact (code-zero)s
     return SD == MOEQ_F16 ? (float)(_Float16)v : v;                 // bf16: rounded at pack
 }
 
-// Eight words (rows k..k+7 of one word column) -> eight bf16x8 B operands.
-template <int SD>
-__device__ __forceinline__ void dequant_operands(const uint32_t wd[8], const GroupConst<SD> &gc,
-                                                 bf16x8 bop[8]) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        float q0[8], q1[8];
-        decode_codes(wd[2 * p], q0);
-        decode_codes(wd[2 * p + 1], q1);
-#pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
-            bop[sl][2 * p] = (__bf16)coeff<SD>(q0[sl], gc, sl);
-            bop[sl][2 * p + 1] = (__bf16)coeff<SD>(q1[sl], gc, sl);
-        }
-    }
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});  // v_cvt_pk_bf16_f32
 }
 
 __device__ __forceinline__ float swiglu_f(float g, float u, float clamp, float alpha, float off) {
@@ -118,11 +87,67 @@ __device__ __forceinline__ float swiglu_f(float g, float u, float clamp, float a
     return g * (1.0f / (1.0f + expf(-alpha * g))) * (u + off);
 }
 
+constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 buffer descriptor, 32-bit data
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, size_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)(uint32_t)bytes,
+                                             kRawBufferWord3);
+}
+
+// Raw per-group words of one operand: the zero word and 8 scales.
+template <int SD>
+struct GroupRaw {
+    uint32_t zw;
+    u32x4 s0, s1;  // s1 only for fp32 scales
+};
+
+template <int SD>
+__device__ __forceinline__ void load_group_raw(__amdgpu_buffer_rsrc_t rz, __amdgpu_buffer_rsrc_t rs,
+                                               int voff_z, int voff_s, int gi, int W, int N,
+                                               GroupRaw<SD> &r) {
+    constexpr int sb = SD == MOEQ_F32 ? 4 : 2;
+    r.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, voff_z, gi * W * 4, 0);
+    r.s0 = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_s, gi * N * sb, 0);
+    if (SD == MOEQ_F32) r.s1 = __builtin_amdgcn_raw_buffer_load_b128(rs, voff_s + 16, gi * N * sb, 0);
+}
+
+template <int SD>
+__device__ __forceinline__ void decode_group(const GroupRaw<SD> &r, GroupConst<SD> &gc) {
+    float z[8], sv[8];
+    decode_codes(r.zw, z);  // zero * 2^-9
+    if (SD == MOEQ_F32) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            sv[c] = __uint_as_float(r.s0[c]);
+            sv[4 + c] = __uint_as_float(r.s1[c]);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t v = r.s0[c];
+            if (SD == MOEQ_BF16) {
+                sv[2 * c] = __uint_as_float(v << 16);
+                sv[2 * c + 1] = __uint_as_float(v & 0xFFFF0000u);
+            } else {
+                sv[2 * c] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+                sv[2 * c + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+            }
+        }
+    }
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+        const float sc = sv[kSlotCol[sl]];
+        gc.s[sl] = sc * kCodeUnit;                                          // exact
+        gc.zs[sl] = SD == MOEQ_F32 ? z[sl] : -(z[sl] * kCodeUnit) * sc;    // exact: 4 x 16 bits
+    }
+}
+
 struct StreamArgs {
     const __bf16 *in;         // [A, K] rows sorted by expert
-    __bf16 *out;              // [A, Nout]
+    __bf16 *out;              // [A, N]
     const int32_t *offsets;   // [E+1]
-    int K, W, strips, g;      // W = N/8 words per weight row, strips = W/16
+    int K, W, g;              // W = N/8 words per weight row
+    int parts;                // column parts per expert (blocks per expert)
     const uint32_t *qw[2];
     const uint32_t *qz[2];
     const void *sc[2];
@@ -131,142 +156,286 @@ struct StreamArgs {
 };
 
 // ------------------------------------------------------------------ stream
-// Weight-streaming kernel for few rows per expert (decode).  Block = one
-// expert x one strip of 16 word columns (128 output columns) of each operand
-// set (gate and up, or the single down cube).  Its KSPLIT waves split K; each
-// wave streams its K range once, decoding into registers, and multiplies it
-// against RT x 16 rows.  Partial sums meet in LDS in a fixed order, then wave
-// 0 applies bias, storage rounding and SwiGLU and stores.
-template <int NSETS, int SD, int KSPLIT, int RT>
-__global__ __launch_bounds__(64 * KSPLIT) void awq_stream_kernel(StreamArgs a) {
-    constexpr int NACC = NSETS * 8 * RT;
-    __shared__ f32x4 red[KSPLIT > 1 ? KSPLIT / 2 : 1][NACC][kWave];
-    const int e = blockIdx.x / a.strips, strip = blockIdx.x % a.strips;
+// Weight-streaming kernel for few rows per expert (decode).
+//
+// Block = one expert x one column part of SPW strips (a strip = 16 word
+// columns = 128 output columns).  Its waves are NSETS x SPW x KSPLIT: wave
+// (set, strip, q) streams one strip of one cube (gate or up, or the single
+// down cube) over K slice q.  The waves of a block advance in lockstep (a
+// barrier per 128-row group), so the CU reads each row block of its part as
+// one contiguous piece -- one wave per strip would leave every row split over
+// several XCDs and halve the achieved bandwidth.
+//
+// Per wave and 32-row step: eight buffer loads of one word per lane (row
+// offsets are scalar), nibble planes, codes through the fp8 converter, one fma
+// per coefficient, one pack per pair, 8 MFMAs per 16-row tile.  Steps run
+// DEPTH ahead; the K slices meet in LDS in a fixed order; the up results join
+// the gate results in LDS for the bias / storage rounding / SwiGLU epilogue.
+template <int RT>
+constexpr int stream_waves() { return RT == 1 ? 3 : 2; }
+
+template <int NSETS, int SPW, int KSPLIT>
+constexpr int stream_lds_bufs() {
+    constexpr int tree = NSETS * SPW * (KSPLIT / 2);
+    constexpr int join = NSETS == 2 ? SPW : 0;
+    return tree > join ? tree : (join > 0 ? join : 1);
+}
+
+template <int NSETS, int SD, int SPW, int KSPLIT, int RT, int DEPTH, int SPG>
+__global__ __launch_bounds__(64 * NSETS * SPW * KSPLIT)
+__attribute__((amdgpu_waves_per_eu(stream_waves<RT>(), stream_waves<RT>())))
+void awq_stream_kernel(StreamArgs a) {
+    constexpr int NACC = 8 * RT;
+    constexpr int sb = SD == MOEQ_F32 ? 4 : 2;
+    // LDS: partial sums of the K tree, then the up results for the epilogue
+    __shared__ f32x4 red[stream_lds_bufs<NSETS, SPW, KSPLIT>()][NACC][kWave];
+
+    const int e = blockIdx.x / a.parts, part = blockIdx.x % a.parts;
     const int r0 = a.offsets[e], r1 = a.offsets[e + 1];
     if (r1 <= r0) return;  // untouched expert: no weight bytes are read
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // wave roles as scalars: keeps every K offset (buffer soffset) in SGPRs
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q = wv % KSPLIT, unit = wv / KSPLIT;  // unit = (set, strip)
+    const int strip = unit % SPW, set = unit / SPW;
+    const int lane = threadIdx.x & 63;
     const int c = lane & 15, grp = lane >> 4;
-    const int j = strip * 16 + c;
-    const int Kw = a.K / KSPLIT;
-    const int kbeg = w * Kw, kend = kbeg + Kw;
-    const int G = a.K / a.g;
-    const int N = a.W * 8;
+    const int j = (part * SPW + strip) * 16 + c;  // this lane's word column
+    const int K = a.K, W = a.W, N = W * 8, g = a.g, G = K / g;
+    const int Kw = K / KSPLIT;
+    const int kbeg = q * Kw, kend = kbeg + Kw;
+
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.qw[set] + (size_t)e * K * W, (size_t)K * W * 4);
+    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(a.qz[set] + (size_t)e * G * W, (size_t)G * W * 4);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
+        static_cast<const char *>(a.sc[set]) + (size_t)e * G * N * sb, (size_t)G * N * sb);
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a.in, (size_t)r1 * K * 2);
+    const int voff_w = (grp * 8 * W + j) * 4;
+    const int voff_z = j * 4, voff_s = 8 * j * sb;
 
     for (int m0 = r0; m0 < r1; m0 += 16 * RT) {
-        f32x4 acc[NSETS][8][RT];
+        int voff_a[RT];
 #pragma unroll
-        for (int s = 0; s < NSETS; ++s)
+        for (int rt = 0; rt < RT; ++rt) {
+            const int row = m0 + rt * 16 + c;
+            voff_a[rt] = row < r1 ? (row * K + grp * 8) * 2 : 0x7fffffff;  // past end: zeros
+        }
+        f32x4 acc[8][RT];
 #pragma unroll
-            for (int sl = 0; sl < 8; ++sl)
+        for (int sl = 0; sl < 8; ++sl)
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) acc[s][sl][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        GroupConst<SD> gc[NSETS];
-        int cur = -1;
-        for (int k0 = kbeg; k0 < kend; k0 += 32) {
-            const int gi = k0 / a.g;
-            if (gi != cur) {
+            for (int rt = 0; rt < RT; ++rt) acc[sl][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        GroupRaw<SD> graw;
+        GroupConst<SD> gc;
+        // One 32-row step: nibble planes of the eight words, then (refill hook:
+        // the words are dead from here) codes, coefficients, packs and MFMAs.
+        auto step = [&](const uint32_t wd[8], const bf16x8 av[RT], auto &&refill_words) {
+            uint32_t lo[8], hi[8];
 #pragma unroll
-                for (int s = 0; s < NSETS; ++s)
-                    load_group<SD>(a.qz[s], a.sc[s], ((size_t)e * G + gi) * a.W + j,
-                                   ((size_t)e * G + gi) * N + 8 * j, gc[s]);
-                cur = gi;
+            for (int i = 0; i < 8; ++i) {
+                lo[i] = and_opaque(wd[i], 0x0F0F0F0Fu);
+                hi[i] = and_opaque(wd[i] >> 4, 0x0F0F0F0Fu);
             }
-            uint32_t wd[NSETS][8];
-            const size_t wrow = ((size_t)e * a.K + k0 + grp * 8) * a.W + j;
+            refill_words();
 #pragma unroll
-            for (int s = 0; s < NSETS; ++s)
+            for (int pr = 0; pr < 4; ++pr) {  // slot pair (2pr, 2pr+1)
+                f32x2 qv[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) wd[s][i] = a.qw[s][wrow + (size_t)i * a.W];
-            bf16x8 av[RT];
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t v = pr < 2 ? lo[i] : hi[i];
+                    qv[i] = (pr & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(v, true)
+                                     : __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
+                }
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const int row = m0 + rt * 16 + c;
-                if (row < r1)
-                    av[rt] = *reinterpret_cast<const bf16x8 *>(a.in + (size_t)row * a.K + k0 +
-                                                               grp * 8);
-                else
-                    av[rt] = bf16x8{};
-            }
+                for (int h = 0; h < 2; ++h) {
+                    const int sl = 2 * pr + h;
+                    u32x4 op;
 #pragma unroll
-            for (int s = 0; s < NSETS; ++s) {
-                bf16x8 bop[8];
-                dequant_operands<SD>(wd[s], gc[s], bop);
-#pragma unroll
-                for (int sl = 0; sl < 8; ++sl)
+                    for (int p = 0; p < 4; ++p)
+                        op[p] = pack_bf16(coeff<SD>(qv[2 * p][h], gc, sl),
+                                          coeff<SD>(qv[2 * p + 1][h], gc, sl));
+                    const bf16x8 bop = __builtin_bit_cast(bf16x8, op);
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt)
-                        acc[s][sl][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            av[rt], bop[sl], acc[s][sl][rt], 0, 0, 0);
+                        acc[sl][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[rt], bop,
+                                                                              acc[sl][rt], 0, 0, 0);
+                }
+            }
+        };
+
+        if constexpr (SPG > 0) {
+            // Branch-free pipeline: groups of SPG steps, steps unrolled, DEPTH
+            // steps in flight in a fixed register ring (slot t % DEPTH).  Loads
+            // past the wave's K range get an out-of-range offset (the buffer
+            // unit returns zeros without a memory access), so every load is
+            // issued unconditionally and the wait counts stay exact.  Each issue
+            // is pinned by a scheduling barrier: the scheduler would otherwise
+            // sink the prefetch next to its use.
+            static_assert(SPG % DEPTH == 0 && SPG >= DEPTH, "ring must tile a group");
+            uint32_t wd[DEPTH][8];
+            bf16x8 av[DEPTH][RT];
+            constexpr int kOff = 0x40000000;  // beyond any cube: reads as zero
+            auto issue_words = [&](int st, int kk) {
+                const bool on = kk < kend;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    wd[st][i] = __builtin_amdgcn_raw_buffer_load_b32(
+                        rw, voff_w, on ? (kk + i) * W * 4 : kOff, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            auto issue_rows = [&](int st, int kk) {
+                const bool on = kk < kend;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    av[st][rt] = __builtin_bit_cast(
+                        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, voff_a[rt],
+                                                                      on ? kk * 2 : kOff, 0));
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            const int gbeg = kbeg / g, gend = kend / g;
+            load_group_raw<SD>(rz, rs, voff_z, voff_s, gbeg, W, N, graw);
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                issue_words(d, kbeg + 32 * d);
+                issue_rows(d, kbeg + 32 * d);
+            }
+            for (int gi = gbeg; gi < gend; ++gi) {
+                __syncthreads();  // lockstep: the block reads one row block at a time
+                decode_group<SD>(graw, gc);
+#pragma unroll
+                for (int t = 0; t < SPG; ++t) {
+                    const int d = t % DEPTH;
+                    const int kn = gi * g + 32 * (t + DEPTH);
+                    if (t == SPG - DEPTH) {
+                        // next group's constants, decoded DEPTH steps from now
+                        load_group_raw<SD>(rz, rs, voff_z, voff_s, gi + 1 < gend ? gi + 1 : gi,
+                                           W, N, graw);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    step(wd[d], av[d], [&] { issue_words(d, kn); });
+                    issue_rows(d, kn);
+                }
+            }
+        } else {
+            // General K ranges and group sizes: one step in flight, a lockstep
+            // barrier every 4 steps (every wave runs the same number of steps).
+            uint32_t wd[8], wn[8];
+            bf16x8 av[RT], an[RT];
+            load_group_raw<SD>(rz, rs, voff_z, voff_s, kbeg / g, W, N, graw);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                wd[i] = __builtin_amdgcn_raw_buffer_load_b32(rw, voff_w, (kbeg + i) * W * 4, 0);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                av[rt] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, voff_a[rt], kbeg * 2, 0));
+            int it = 0;
+            for (int k0 = kbeg; k0 < kend; k0 += 32, ++it) {
+                if ((it & 3) == 0) __syncthreads();
+                if (k0 == kbeg || k0 % g == 0) decode_group<SD>(graw, gc);
+                const int kn = k0 + 32;
+                if (kn < kend) {
+                    if (kn % g == 0) load_group_raw<SD>(rz, rs, voff_z, voff_s, kn / g, W, N, graw);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        wn[i] = __builtin_amdgcn_raw_buffer_load_b32(rw, voff_w, (kn + i) * W * 4, 0);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        an[rt] = __builtin_bit_cast(
+                            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, voff_a[rt], kn * 2, 0));
+                }
+                step(wd, av, [] {});
+                if (kn < kend) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) wd[i] = wn[i];
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) av[rt] = an[rt];
+                }
             }
         }
-        // fixed-order tree over the K split: w0 = (w0 + w2) + (w1 + w3)
-        if (KSPLIT > 1) {
+
+        // fixed-order tree over the K slices of each (set, strip):
+        // q0 = (q0 + q2) + (q1 + q3)
+        if constexpr (KSPLIT > 1) {
 #pragma unroll
             for (int half = KSPLIT / 2; half >= 1; half >>= 1) {
                 __syncthreads();
-                if (w >= half && w < 2 * half) {
+                if (q >= half && q < 2 * half) {
+                    const int b = unit * (KSPLIT / 2) + (q - half);
 #pragma unroll
-                    for (int s = 0; s < NSETS; ++s)
+                    for (int sl = 0; sl < 8; ++sl)
 #pragma unroll
-                        for (int sl = 0; sl < 8; ++sl)
-#pragma unroll
-                            for (int rt = 0; rt < RT; ++rt)
-                                red[w - half][(s * 8 + sl) * RT + rt][lane] = acc[s][sl][rt];
+                        for (int rt = 0; rt < RT; ++rt) red[b][sl * RT + rt][lane] = acc[sl][rt];
                 }
                 __syncthreads();
-                if (w < half) {
+                if (q < half) {
+                    const int b = unit * (KSPLIT / 2) + q;
 #pragma unroll
-                    for (int s = 0; s < NSETS; ++s)
+                    for (int sl = 0; sl < 8; ++sl)
 #pragma unroll
-                        for (int sl = 0; sl < 8; ++sl)
-#pragma unroll
-                            for (int rt = 0; rt < RT; ++rt)
-                                acc[s][sl][rt] += red[w][(s * 8 + sl) * RT + rt][lane];
+                        for (int rt = 0; rt < RT; ++rt) acc[sl][rt] += red[b][sl * RT + rt][lane];
                 }
             }
         }
-        if (w != 0) continue;
+        if constexpr (NSETS == 2) {
+            // up results (set 1) join the gate results (set 0) of the same strip
+            __syncthreads();
+            if (q == 0 && set == 1) {
 #pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
-            const int col = 8 * j + kSlotCol[sl];
-            float b0 = 0.f, b1 = 0.f;
-            if (a.bias[0]) b0 = load_f<SD>(a.bias[0], (size_t)e * N + col);
-            if (NSETS == 2 && a.bias[1]) b1 = load_f<SD>(a.bias[1], (size_t)e * N + col);
+                for (int sl = 0; sl < 8; ++sl)
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+                    for (int rt = 0; rt < RT; ++rt) red[strip][sl * RT + rt][lane] = acc[sl][rt];
+            }
+            __syncthreads();
+        }
+        if (q == 0 && set == 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = m0 + rt * 16 + grp * 4 + i;
-                    if (row >= r1) continue;
-                    float v;
-                    if (NSETS == 2) {
-                        const float g = round_to<MOEQ_BF16>(acc[0][sl][rt][i] + b0);
-                        const float u = round_to<MOEQ_BF16>(acc[1][sl][rt][i] + b1);
-                        v = swiglu_f(g, u, a.clamp, a.alpha, a.up_offset);
-                    } else {
-                        v = acc[0][sl][rt][i] + b0;
+            for (int sl = 0; sl < 8; ++sl) {
+                const int col = 8 * j + kSlotCol[sl];
+                float b0 = 0.f, b1 = 0.f;
+                if (a.bias[0]) b0 = load_f<SD>(a.bias[0], (size_t)e * N + col);
+                if (NSETS == 2 && a.bias[1]) b1 = load_f<SD>(a.bias[1], (size_t)e * N + col);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    f32x4 up4 = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (NSETS == 2) up4 = red[strip][sl * RT + rt][lane];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = m0 + rt * 16 + grp * 4 + i;
+                        if (row >= r1) continue;
+                        float v;
+                        if (NSETS == 2) {
+                            const float gv = round_to<MOEQ_BF16>(acc[sl][rt][i] + b0);
+                            const float uv = round_to<MOEQ_BF16>(up4[i] + b1);
+                            v = swiglu_f(gv, uv, a.clamp, a.alpha, a.up_offset);
+                        } else {
+                            v = acc[sl][rt][i] + b0;
+                        }
+                        a.out[(size_t)row * N + col] = (__bf16)v;
                     }
-                    a.out[(size_t)row * N + col] = (__bf16)v;
                 }
+            }
         }
     }
 }
 
-template <int NSETS, int SD>
-hipError_t launch_stream(const StreamArgs &a, int E, int ksplit, int rt, hipStream_t s) {
-    dim3 grid(E * a.strips);
-#define MOEQ_STREAM(KS, RTT)                                                                  \
-    if (ksplit == KS && rt == RTT) {                                                          \
-        hipLaunchKernelGGL((awq_stream_kernel<NSETS, SD, KS, RTT>), grid, dim3(64 * KS), 0, s, \
-                           a);                                                                \
-        return hipGetLastError();                                                             \
+template <int NSETS, int SD, int SPW>
+hipError_t launch_stream(const StreamArgs &a, int E, int ksplit, int rt, int depth,
+                         hipStream_t s) {
+    dim3 grid(E * a.parts);
+#define MOEQ_STREAM(KS, RTT, D, SP)                                                          \
+    if (ksplit == KS && rt == RTT && depth == D) {                                           \
+        hipLaunchKernelGGL((awq_stream_kernel<NSETS, SD, SPW, KS, RTT, D, SP>), grid,        \
+                           dim3(64 * NSETS * SPW * KS), 0, s, a);                            \
+        return hipGetLastError();                                                            \
     }
-    MOEQ_STREAM(4, 1)
-    MOEQ_STREAM(4, 2)
-    MOEQ_STREAM(2, 1)
-    MOEQ_STREAM(2, 2)
-    MOEQ_STREAM(1, 1)
-    MOEQ_STREAM(1, 2)
+    if constexpr (NSETS * SPW * 2 <= 12) {
+        MOEQ_STREAM(2, 1, 2, 4)
+        MOEQ_STREAM(2, 1, 1, 0)
+    }
+    MOEQ_STREAM(1, 1, 2, 4)
+    MOEQ_STREAM(1, 1, 1, 0)
+    MOEQ_STREAM(1, 2, 1, 0)
 #undef MOEQ_STREAM
     return hipErrorInvalidValue;
 }
@@ -275,6 +444,7 @@ hipError_t launch_stream(const StreamArgs &a, int E, int ksplit, int rt, hipStre
 bool stream_fits(const ProjProblem &p) {
     if (p.act != MOEQ_BF16 || p.w0.format != MOEQ_FMT_AWQ || !p.offsets) return false;
     if (p.w0.N % 128 != 0 || p.w0.K % 32 != 0 || p.w0.g % 32 != 0) return false;
+    if ((size_t)p.rows * p.w0.K * 2 >= ((size_t)1 << 31)) return false;
     const double rows_per_expert = (double)p.rows / (double)p.E;
     return rows_per_expert <= 24.0;
 }
@@ -287,7 +457,6 @@ hipError_t run_stream(const ProjProblem &p, hipStream_t s) {
     a.offsets = p.offsets;
     a.K = p.w0.K;
     a.W = p.w0.N / 8;
-    a.strips = a.W / 16;
     a.g = p.w0.g;
     const PackedOperand *ops[2] = {&p.w0, &p.w1};
     for (int i = 0; i < 2; ++i) {
@@ -299,14 +468,50 @@ hipError_t run_stream(const ProjProblem &p, hipStream_t s) {
     a.clamp = p.clamp;
     a.alpha = p.alpha;
     a.up_offset = p.up_offset;
-    // split K four ways when each quarter is whole 32-row steps
-    const int ksplit = (a.K % 128 == 0) ? 4 : (a.K % 64 == 0 ? 2 : 1);
+    const int strips = a.W / 16;
+    // rows: one 16-row tile unless experts average more than 8 rows
     const int rt = ((double)p.rows / (double)p.E) <= 8.0 ? 1 : 2;
-    switch (p.w0.sdt) {
-    case MOEQ_BF16: return launch_stream<NSETS, MOEQ_BF16>(a, p.E, ksplit, rt, s);
-    case MOEQ_F16: return launch_stream<NSETS, MOEQ_F16>(a, p.E, ksplit, rt, s);
-    default: return launch_stream<NSETS, MOEQ_F32>(a, p.E, ksplit, rt, s);
+    // columns: a block's part is as wide as possible while E * parts still
+    // covers the 256 CUs; two operand sets take 3-strip parts, one set 8
+    int spw;
+    if (NSETS == 2)
+        spw = strips % 3 == 0 ? 3 : (strips % 2 == 0 ? 2 : 1);
+    else
+        spw = strips % 8 == 0 ? 8 : (strips % 4 == 0 ? 4 : (strips % 2 == 0 ? 2 : 1));
+    if (const char *v = getenv("MOEQ_STREAM_SPW")) {  // tuning override (launch shape only)
+        const int x = atoi(v);
+        if ((x == 1 || x == 2 || x == 3 || x == 4 || x == 8) && strips % x == 0) spw = x;
     }
+    // K split: two ways when the block stays within 12 waves (3 per SIMD, all
+    // unspilled) and each half is whole groups
+    int ksplit = (NSETS * spw * 2 <= 12 && (a.K / a.g) % 2 == 0) ? 2 : 1;
+    if (rt == 2) ksplit = 1;
+    if (const char *v = getenv("MOEQ_STREAM_KSPLIT")) {
+        const int x = atoi(v);
+        if ((x == 1 || x == 2) && NSETS * spw * x <= 12 && a.K % (32 * x) == 0 && rt == 1)
+            ksplit = x;
+    }
+    // the pipelined variant needs 128-row groups and group-aligned K slices
+    int depth = (rt == 1 && a.g == 128 && (a.K / ksplit) % a.g == 0) ? 2 : 1;
+    if (const char *v = getenv("MOEQ_STREAM_DEPTH"))
+        if (atoi(v) == 1) depth = 1;
+    a.parts = strips / spw;
+#define MOEQ_SPW(X)                                                                             \
+    case X:                                                                                     \
+        switch (p.w0.sdt) {                                                                     \
+        case MOEQ_BF16: return launch_stream<NSETS, MOEQ_BF16, X>(a, p.E, ksplit, rt, depth, s); \
+        case MOEQ_F16: return launch_stream<NSETS, MOEQ_F16, X>(a, p.E, ksplit, rt, depth, s);   \
+        default: return launch_stream<NSETS, MOEQ_F32, X>(a, p.E, ksplit, rt, depth, s);         \
+        }
+    switch (spw) {
+        MOEQ_SPW(1)
+        MOEQ_SPW(2)
+        MOEQ_SPW(3)
+        MOEQ_SPW(4)
+        MOEQ_SPW(8)
+    default: return hipErrorInvalidValue;
+    }
+#undef MOEQ_SPW
 }
 
 }  // namespace
