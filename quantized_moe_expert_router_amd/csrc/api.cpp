@@ -230,6 +230,11 @@ moeq_status moe_dispatch(const void *x, moeq_dtype act, int32_t T, int32_t K,
     if (!x || !logits || !values || !weights || !selected || !row_experts)
         return fail(MOEQ_EINVAL, "NULL tensor pointer");
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (small_dispatch_fits(T, E, top_k, row_bytes, x, values))  // one launch for small batches
+        return device_status(launch_dispatch_small(x, row_bytes, logits, expert_bias, T, E, top_k,
+                                                   values, weights, selected, row_experts, route,
+                                                   s),
+                             "dispatch");
     if ((st = device_status(launch_router(logits, expert_bias, T, E, top_k, selected, weights, s),
                             "router")) != MOEQ_OK)
         return st;

@@ -148,6 +148,8 @@ struct StreamArgs {
     const int32_t *offsets;   // [E+1]
     int K, W, g;              // W = N/8 words per weight row
     int parts;                // column parts per expert (blocks per expert)
+    int E;                    // experts
+    int xcd_pairs;            // 1: the parts of an expert share an XCD (see kernel)
     const uint32_t *qw[2];
     const uint32_t *qz[2];
     const void *sc[2];
@@ -190,7 +192,20 @@ void awq_stream_kernel(StreamArgs a) {
     // LDS: partial sums of the K tree, then the up results for the epilogue
     __shared__ f32x4 red[stream_lds_bufs<NSETS, SPW, KSPLIT>()][NACC][kWave];
 
-    const int e = blockIdx.x / a.parts, part = blockIdx.x % a.parts;
+    // Blocks are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8).
+    // With xcd_pairs, block b = 8 * (P * n + part) + x holds expert 8n + x,
+    // part `part`: the P parts of an expert run on one XCD, launched together,
+    // so its L2 sees whole rows.
+    int e, part;
+    if (a.xcd_pairs) {
+        const int x = blockIdx.x % 8, idx = blockIdx.x / 8;
+        e = (idx / a.parts) * 8 + x;
+        part = idx % a.parts;
+        if (e >= a.E) return;
+    } else {
+        e = blockIdx.x / a.parts;
+        part = blockIdx.x % a.parts;
+    }
     const int r0 = a.offsets[e], r1 = a.offsets[e + 1];
     if (r1 <= r0) return;  // untouched expert: no weight bytes are read
     // wave roles as scalars: keeps every K offset (buffer soffset) in SGPRs
@@ -422,7 +437,7 @@ void awq_stream_kernel(StreamArgs a) {
 template <int NSETS, int SD, int SPW>
 hipError_t launch_stream(const StreamArgs &a, int E, int ksplit, int rt, int depth,
                          hipStream_t s) {
-    dim3 grid(E * a.parts);
+    dim3 grid(a.xcd_pairs ? ((E + 7) / 8) * 8 * a.parts : E * a.parts);
 #define MOEQ_STREAM(KS, RTT, D, SP)                                                          \
     if (ksplit == KS && rt == RTT && depth == D) {                                           \
         hipLaunchKernelGGL((awq_stream_kernel<NSETS, SD, SPW, KS, RTT, D, SP>), grid,        \
@@ -430,9 +445,11 @@ hipError_t launch_stream(const StreamArgs &a, int E, int ksplit, int rt, int dep
         return hipGetLastError();                                                            \
     }
     if constexpr (NSETS * SPW * 2 <= 12) {
+        MOEQ_STREAM(2, 1, 4, 4)
         MOEQ_STREAM(2, 1, 2, 4)
         MOEQ_STREAM(2, 1, 1, 0)
     }
+    MOEQ_STREAM(1, 1, 4, 4)
     MOEQ_STREAM(1, 1, 2, 4)
     MOEQ_STREAM(1, 1, 1, 0)
     MOEQ_STREAM(1, 2, 1, 0)
@@ -493,9 +510,14 @@ hipError_t run_stream(const ProjProblem &p, hipStream_t s) {
     }
     // the pipelined variant needs 128-row groups and group-aligned K slices
     int depth = (rt == 1 && a.g == 128 && (a.K / ksplit) % a.g == 0) ? 2 : 1;
-    if (const char *v = getenv("MOEQ_STREAM_DEPTH"))
-        if (atoi(v) == 1) depth = 1;
+    if (const char *v = getenv("MOEQ_STREAM_DEPTH")) {
+        const int x = atoi(v);
+        if (x == 1 || (depth > 1 && (x == 2 || x == 4))) depth = x;
+    }
     a.parts = strips / spw;
+    a.E = p.E;
+    a.xcd_pairs = 1;
+    if (const char *v = getenv("MOEQ_STREAM_XCD")) a.xcd_pairs = atoi(v) != 0;
 #define MOEQ_SPW(X)                                                                             \
     case X:                                                                                     \
         switch (p.w0.sdt) {                                                                     \

@@ -52,6 +52,11 @@ enum ProjMode {
 
 hipError_t launch_router(const float *logits, const float *bias, int T, int E, int k,
                          uint32_t *selected, float *weights, hipStream_t s);
+bool small_dispatch_fits(int T, int E, int k, size_t row_bytes, const void *x, const void *values);
+hipError_t launch_dispatch_small(const void *x, size_t row_bytes, const float *logits,
+                                 const float *bias, int T, int E, int k, void *values,
+                                 float *weights, uint32_t *selected, uint32_t *row_experts,
+                                 const moeq_route *route, hipStream_t s);
 hipError_t launch_dispatch_index(const uint32_t *selected, int T, int E, int k,
                                  const moeq_route *route, uint32_t *row_experts,
                                  hipStream_t s);

@@ -12,97 +12,272 @@
 namespace moeq {
 
 // ------------------------------------------------------------------ router
-// One wave per token.  Lane l holds the scores of experts l, l+64, ...
-// Selection: k rounds of a wave-wide argmax over the untaken experts, ordered
-// by (score descending, expert ID ascending).  Slot j keeps the j-th winner.
-// Weights: softmax over the k selected scores in double, rounded to fp32.
-struct Cand {
-    float v;
-    int e;  // kNone when the lane has no candidate
-};
-constexpr int kNone = 0x7fffffff;
+// Selection key: one 64-bit integer per (score, expert) whose unsigned order is
+// the selection order -- score descending, then expert ID ascending.  High
+// word: the score's bits made order-preserving (-0 is first turned into +0,
+// since equal scores tie); low word: the inverted expert ID.  Key 0 marks an
+// expert that is already taken or absent.  Scores are finite (no NaN).
+__device__ __forceinline__ uint64_t sel_key(float score, int e) {
+    uint32_t u = __float_as_uint(score + 0.0f);          // -0 + 0 = +0
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);      // monotone in the float order
+    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
+}
+__device__ __forceinline__ int key_expert(uint64_t key) { return (int)~(uint32_t)key; }
+__device__ __forceinline__ float key_score(uint64_t key) {
+    uint32_t u = (uint32_t)(key >> 32);
+    u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+    return __uint_as_float(u);
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-__device__ __forceinline__ bool better(const Cand &a, const Cand &b) {
-    if (a.e == kNone) return false;
-    if (b.e == kNone) return true;
-    return a.v > b.v || (a.v == b.v && a.e < b.e);
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_key(uint64_t v) {
+    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-template <int EPL>
-__global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ logits,
-                                                          const float *__restrict__ bias,
-                                                          int T, int E, int k,
-                                                          uint32_t *__restrict__ selected,
-                                                          float *__restrict__ weights) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) / kWave);
-    if (t >= T) return;  // uniform per wave
+// Max key over the 16 lanes of a DPP row: four rotations (row_ror 8, 4, 2, 1)
+// leave the row maximum in every lane of the row.
+__device__ __forceinline__ uint64_t row16_max(uint64_t k) {
+    k = umax64(k, dpp_key<0x128>(k));
+    k = umax64(k, dpp_key<0x124>(k));
+    k = umax64(k, dpp_key<0x122>(k));
+    k = umax64(k, dpp_key<0x121>(k));
+    return k;
+}
+
+// Routes token t with the LANES lanes of the calling group (16: a DPP row; 64:
+// the whole wave, rows joined by two cross-row shuffles).  Lane r holds the
+// scores of experts r, r+LANES, ...; each of the k rounds takes the group-wide
+// maximum key, and its owner lane clears it.  Lane j < k receives slot j: its
+// expert and its weight, the softmax over the k selected scores evaluated in
+// double in slot order and rounded once to fp32.
+template <int LANES, int EPL>
+__device__ __forceinline__ void route_token(const float *__restrict__ logits,
+                                            const float *__restrict__ bias, int t, int E, int k,
+                                            int r, int group_base_lane, int *sel_out,
+                                            float *w_out) {
     const float *row = logits + (size_t)t * E;
-    float s[EPL];
-    uint32_t taken = 0;
+    uint64_t key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-        const int e = lane + kWave * i;
+        const int e = r + LANES * i;
         if (e < E) {
             float v = row[e];
             if (bias) v = v + bias[e];  // one IEEE fp32 add
-            s[i] = v;
+            key[i] = sel_key(v, e);
         } else {
-            s[i] = 0.0f;
-            taken |= 1u << i;
+            key[i] = 0;
         }
     }
-    int my_sel = 0;
-    float my_score = 0.0f;
+    uint64_t mine = 0;
     for (int j = 0; j < k; ++j) {
-        Cand c{0.0f, kNone};
+        uint64_t best = 0;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            if (!((taken >> i) & 1u)) {
-                Cand d{s[i], lane + kWave * i};
-                if (better(d, c)) c = d;
-            }
+        for (int i = 0; i < EPL; ++i) best = umax64(best, key[i]);
+        best = row16_max(best);
+        if (LANES == 64) {
+            best = umax64(best, __shfl_xor(best, 16));
+            best = umax64(best, __shfl_xor(best, 32));
         }
 #pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) {
-            Cand o{__shfl_xor(c.v, off), __shfl_xor(c.e, off)};
-            if (better(o, c)) c = o;
-        }
-        // every lane now holds the same winner
-        if ((c.e & (kWave - 1)) == lane) taken |= 1u << (c.e / kWave);
-        if (lane == j) {
-            my_sel = c.e;
-            my_score = c.v;
-        }
+        for (int i = 0; i < EPL; ++i) key[i] = key[i] == best ? 0 : key[i];  // taken
+        mine = r == j ? best : mine;
     }
-    const double m = (double)__shfl(my_score, 0);
+    const float my_score = key_score(mine);
+    const double m = (double)__shfl(my_score, group_base_lane);
     const double ex = exp((double)my_score - m);
     double den = 0.0;
-    for (int j = 0; j < k; ++j) den += __shfl(ex, j);  // slot order, same in all lanes
-    if (lane < k) {
-        selected[(size_t)t * k + lane] = (uint32_t)my_sel;
-        weights[(size_t)t * k + lane] = (float)(ex / den);
+    for (int j = 0; j < k; ++j) den += __shfl(ex, group_base_lane + j);  // slot order
+    *sel_out = key_expert(mine);
+    *w_out = (float)(ex / den);
+}
+
+template <int LANES, int EPL>
+__global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ logits,
+                                                     const float *__restrict__ bias, int T, int E,
+                                                     int k, uint32_t *__restrict__ selected,
+                                                     float *__restrict__ weights) {
+    const int t = (int)((blockIdx.x * blockDim.x + threadIdx.x) / LANES);
+    const int r = threadIdx.x % LANES;
+    if (t >= T) return;  // uniform per group
+    int sel;
+    float w;
+    route_token<LANES, EPL>(logits, bias, t, E, k, r, (int)(threadIdx.x & 63) & ~(LANES - 1),
+                            &sel, &w);
+    if (r < k) {
+        selected[(size_t)t * k + r] = (uint32_t)sel;
+        weights[(size_t)t * k + r] = w;
     }
 }
 
 hipError_t launch_router(const float *logits, const float *bias, int T, int E, int k,
                          uint32_t *selected, float *weights, hipStream_t s) {
-    const int waves_per_block = 4;
-    dim3 grid((T + waves_per_block - 1) / waves_per_block), block(waves_per_block * kWave);
-    const int epl = (E + kWave - 1) / kWave;
-#define MOEQ_ROUTER(N)                                                                  \
-    if (epl <= N) {                                                                     \
-        hipLaunchKernelGGL(router_topk_kernel<N>, grid, block, 0, s, logits, bias, T, E, \
-                           k, selected, weights);                                       \
-        return hipGetLastError();                                                       \
+    // 16 lanes per token while a lane holds at most 16 experts, else 64
+#define MOEQ_ROUTER(L, N)                                                                \
+    if (L * N >= E && k <= L) {                                                          \
+        dim3 grid((unsigned)(((size_t)T * L + 255) / 256)), block(256);                  \
+        hipLaunchKernelGGL((router_kernel<L, N>), grid, block, 0, s, logits, bias, T, E, k, \
+                           selected, weights);                                          \
+        return hipGetLastError();                                                        \
     }
-    MOEQ_ROUTER(1)
-    MOEQ_ROUTER(2)
-    MOEQ_ROUTER(4)
-    MOEQ_ROUTER(8)
-    MOEQ_ROUTER(16)
-    MOEQ_ROUTER(32)
+    MOEQ_ROUTER(16, 2)
+    MOEQ_ROUTER(16, 8)
+    MOEQ_ROUTER(16, 16)
+    MOEQ_ROUTER(64, 8)
+    MOEQ_ROUTER(64, 16)
+    MOEQ_ROUTER(64, 32)
 #undef MOEQ_ROUTER
+    return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------------ fused small dispatch
+// Whole dispatch in one launch for small batches (T <= 256, T*k <= 4096,
+// E <= 256, top_k <= 16).  Every block routes all T tokens into LDS (the
+// logits are a few tens of KB, L2-resident), builds the stable order there --
+// expert histogram, exclusive scan, and the rank of token t among the tokens
+// of expert e as a popcount over a per-expert token bitmask -- then block 0
+// writes the routing outputs and every block copies its share of rows.
+constexpr int kSmallT = 256, kSmallA = 4096, kSmallE = 256, kSmallK = 16;
+
+template <int EPL>
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(
+    const uint8_t *__restrict__ x, int row_bytes, const float *__restrict__ logits,
+    const float *__restrict__ bias, int T, int E, int k, uint8_t *__restrict__ values,
+    float *__restrict__ weights, uint32_t *__restrict__ selected,
+    uint32_t *__restrict__ row_experts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ row_src_g, int32_t *__restrict__ slot_pos_g) {
+    __shared__ uint16_t sel_s[kSmallA];
+    __shared__ float w_s[kSmallA];
+    __shared__ int32_t rsrc_s[kSmallA];
+    __shared__ int32_t hist_s[kSmallE];
+    __shared__ int32_t off_s[kSmallE + 1];
+    __shared__ unsigned long long mask_s[kSmallE][kSmallT / 64];
+    __shared__ int wave_tot[16];
+    const int tid = threadIdx.x, A = T * k;
+    const int MW = (T + 63) / 64;
+
+    // 1. routing: 64 rows of 16 lanes per pass
+    for (int t0 = 0; t0 < T; t0 += 64) {
+        const int t = t0 + (tid >> 4), r = tid & 15;
+        if (t < T) {
+            int sel;
+            float w;
+            route_token<16, EPL>(logits, bias, t, E, k, r, (tid & 63) & ~15, &sel, &w);
+            if (r < k) {
+                sel_s[t * k + r] = (uint16_t)sel;
+                w_s[t * k + r] = w;
+            }
+        }
+    }
+    for (int e = tid; e < E; e += blockDim.x) {
+        hist_s[e] = 0;
+        for (int mw = 0; mw < MW; ++mw) mask_s[e][mw] = 0ull;
+    }
+    __syncthreads();
+    // 2. histogram and token bitmask per expert
+    for (int a = tid; a < A; a += blockDim.x) {
+        const int e = sel_s[a], t = a / k;
+        atomicAdd(&hist_s[e], 1);
+        atomicOr(&mask_s[e][t >> 6], 1ull << (t & 63));
+    }
+    __syncthreads();
+    // 3. exclusive scan of the histogram (E <= 256 < threads: one element each)
+    {
+        const int lane = tid & 63, wv = tid >> 6;
+        const int v = tid < E ? hist_s[tid] : 0;
+        int incl = v;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int n = __shfl_up(incl, o);
+            if (lane >= o) incl += n;
+        }
+        if (lane == kWave - 1) wave_tot[wv] = incl;
+        __syncthreads();
+        int base = 0;
+        for (int w = 0; w < wv; ++w) base += wave_tot[w];
+        if (tid < E) off_s[tid] = base + incl - v;
+        if (tid == 0) off_s[E] = A;
+    }
+    __syncthreads();
+    // 4. stable positions: rank of token t among the tokens of expert e
+    for (int a = tid; a < A; a += blockDim.x) {
+        const int e = sel_s[a], t = a / k;
+        int rank = __popcll(mask_s[e][t >> 6] & ((1ull << (t & 63)) - 1ull));
+        for (int mw = 0; mw < (t >> 6); ++mw) rank += __popcll(mask_s[e][mw]);
+        const int p = off_s[e] + rank;
+        rsrc_s[p] = t;
+        if (blockIdx.x == 0) {
+            slot_pos_g[a] = p;
+            row_src_g[p] = t;
+            row_experts[p] = (uint32_t)e;
+            selected[a] = (uint32_t)e;
+            weights[a] = w_s[a];
+        }
+    }
+    if (blockIdx.x == 0)
+        for (int e = tid; e <= E; e += blockDim.x) offsets[e] = off_s[e];
+    __syncthreads();
+    // 5. row copies: the grid walks the flattened (row, 16-byte vector) space;
+    //    each thread issues its four loads before its four stores, so the copy
+    //    costs one memory round trip instead of one per row
+    const int vecs = row_bytes / 16;
+    const long total = (long)A * vecs, stride = (long)gridDim.x * blockDim.x * 4;
+    for (long base = (long)blockIdx.x * blockDim.x * 4 + tid; base < total; base += stride) {
+        const long step = blockDim.x;
+        if (base + 3 * step < total) {
+            const uint4 *src[4];
+            uint4 *dst[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const long idx = base + u * step;
+                const int p = (int)(idx / vecs), i = (int)(idx % vecs);
+                src[u] = reinterpret_cast<const uint4 *>(x + (size_t)rsrc_s[p] * row_bytes) + i;
+                dst[u] = reinterpret_cast<uint4 *>(values + (size_t)p * row_bytes) + i;
+            }
+            const uint4 v0 = *src[0], v1 = *src[1], v2 = *src[2], v3 = *src[3];
+            *dst[0] = v0;
+            *dst[1] = v1;
+            *dst[2] = v2;
+            *dst[3] = v3;
+        } else {
+            for (long idx = base; idx < total; idx += step) {
+                const int p = (int)(idx / vecs), i = (int)(idx % vecs);
+                reinterpret_cast<uint4 *>(values + (size_t)p * row_bytes)[i] =
+                    reinterpret_cast<const uint4 *>(x + (size_t)rsrc_s[p] * row_bytes)[i];
+            }
+        }
+    }
+}
+
+bool small_dispatch_fits(int T, int E, int k, size_t row_bytes, const void *x, const void *values) {
+    return T <= kSmallT && T * k <= kSmallA && E <= kSmallE && k <= kSmallK && row_bytes % 16 == 0 &&
+           ((uintptr_t)x | (uintptr_t)values) % 16 == 0 && row_bytes < ((size_t)1 << 30);
+}
+
+hipError_t launch_dispatch_small(const void *x, size_t row_bytes, const float *logits,
+                                 const float *bias, int T, int E, int k, void *values,
+                                 float *weights, uint32_t *selected, uint32_t *row_experts,
+                                 const moeq_route *route, hipStream_t s) {
+    const int A = T * k;
+    // enough blocks that every thread copies four 16-byte vectors (at most 256)
+    const long vecs = (long)A * (long)(row_bytes / 16);
+    long want = (vecs + 1024 * 4 - 1) / (1024 * 4);
+    const int blocks = (int)(want < 1 ? 1 : (want > 256 ? 256 : want));
+    const int epl = (E + 15) / 16;
+#define MOEQ_SMALL(N)                                                                          \
+    if (epl <= N) {                                                                            \
+        hipLaunchKernelGGL(dispatch_small_kernel<N>, dim3(blocks), dim3(1024), 0, s,          \
+                           (const uint8_t *)x, (int)row_bytes, logits, bias, T, E, k,           \
+                           (uint8_t *)values, weights, selected, row_experts,                  \
+                           route->expert_offsets, route->row_src, route->slot_pos);            \
+        return hipGetLastError();                                                              \
+    }
+    MOEQ_SMALL(2)
+    MOEQ_SMALL(8)
+    MOEQ_SMALL(16)
+#undef MOEQ_SMALL
     return hipErrorInvalidValue;
 }
 
@@ -283,12 +458,17 @@ hipError_t launch_copy_rows(const void *x, size_t row_bytes, int A, const int32_
 // ------------------------------------------------------------------ combine
 // One block per token.  The k sorted positions are ranked so that slot a of
 // the shared list is the a-th smallest position, i.e. the a-th smallest expert
-// ID; every column then runs acc = fma(w, y, acc) in that order.
+// ID; every column then runs acc = fma(w, y, acc) in that order.  Each thread
+// owns VEC consecutive columns and moves them as one 16-byte vector.
 template <int ACT>
 __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y,
                                                       const float *__restrict__ weights,
                                                       const int32_t *__restrict__ slot_pos,
-                                                      int T, int k, int K, void *__restrict__ out) {
+                                                      int T, int k, int K, bool vec_ok,
+                                                      void *__restrict__ out) {
+    typedef typename Storage<ACT>::T S;
+    constexpr int VEC = 16 / sizeof(S);
+    typedef S sv __attribute__((ext_vector_type(VEC)));
     __shared__ int pos_s[kMaxTopK];
     __shared__ float w_s[kMaxTopK];
     const int t = blockIdx.x;
@@ -300,11 +480,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
         w_s[rank] = weights[(size_t)t * k + threadIdx.x];
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < K; c += blockDim.x) {
-        float acc = 0.0f;
-        for (int a = 0; a < k; ++a)
-            acc = __builtin_fmaf(w_s[a], load_f<ACT>(y, (size_t)pos_s[a] * K + c), acc);
-        store_f<ACT>(out, (size_t)t * K + c, acc);
+    const S *ys = static_cast<const S *>(y);
+    S *os = static_cast<S *>(out);
+    if (vec_ok) {
+        for (int c = threadIdx.x * VEC; c < K; c += blockDim.x * VEC) {
+            float acc[VEC];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
+            for (int a = 0; a < k; ++a) {
+                const sv yv = *reinterpret_cast<const sv *>(ys + (size_t)pos_s[a] * K + c);
+                const float w = w_s[a];
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[v] = __builtin_fmaf(w, (float)yv[v], acc[v]);
+            }
+            sv o;
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) o[v] = (S)acc[v];
+            *reinterpret_cast<sv *>(os + (size_t)t * K + c) = o;
+        }
+    } else {
+        for (int c = threadIdx.x; c < K; c += blockDim.x) {
+            float acc = 0.0f;
+            for (int a = 0; a < k; ++a)
+                acc = __builtin_fmaf(w_s[a], (float)ys[(size_t)pos_s[a] * K + c], acc);
+            os[(size_t)t * K + c] = (S)acc;
+        }
     }
 }
 
@@ -312,15 +512,20 @@ hipError_t launch_combine(const void *y, int act, const float *weights,
                           const int32_t *slot_pos, int T, int k, int K, void *out,
                           hipStream_t s) {
     if (T == 0) return hipSuccess;
+    const int vec = act == MOEQ_F32 ? 4 : 8;
+    const bool vec_ok = ((uintptr_t)y | (uintptr_t)out) % 16 == 0 && K % vec == 0;
+    int threads = vec_ok ? K / vec : K;
+    threads = threads >= 256 ? 256 : ((threads + 63) / 64) * 64;
+#define MOEQ_COMBINE(DT)                                                                   \
+    hipLaunchKernelGGL(combine_kernel<DT>, dim3(T), dim3(threads), 0, s, y, weights, slot_pos, \
+                       T, k, K, vec_ok, out)
     if (act == MOEQ_F32)
-        hipLaunchKernelGGL(combine_kernel<MOEQ_F32>, dim3(T), dim3(256), 0, s, y, weights,
-                           slot_pos, T, k, K, out);
+        MOEQ_COMBINE(MOEQ_F32);
     else if (act == MOEQ_BF16)
-        hipLaunchKernelGGL(combine_kernel<MOEQ_BF16>, dim3(T), dim3(256), 0, s, y, weights,
-                           slot_pos, T, k, K, out);
+        MOEQ_COMBINE(MOEQ_BF16);
     else
-        hipLaunchKernelGGL(combine_kernel<MOEQ_F16>, dim3(T), dim3(256), 0, s, y, weights,
-                           slot_pos, T, k, K, out);
+        MOEQ_COMBINE(MOEQ_F16);
+#undef MOEQ_COMBINE
     return hipGetLastError();
 }
 
