@@ -79,6 +79,8 @@ typedef struct moeq_route {
     int32_t *row_src;          /* [A]   source token of sorted row p            */
     int32_t *slot_pos;         /* [T*top_k] sorted row of assignment (t, j)     */
     int32_t *block_base;       /* internal [token_blocks*E]                      */
+    int32_t *tile_offsets;     /* internal [E+1] prefix of ceil(rows_e / 128)    */
+    int32_t *tile_expert;      /* internal [ceil(A/128)+E] expert of each m-tile */
     uint32_t magic;            /* set by moeq_route_bind                         */
 } moeq_route;
 

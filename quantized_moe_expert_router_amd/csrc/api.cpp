@@ -50,7 +50,8 @@ bool mul_ok(size_t a, size_t b, size_t *out) {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t off_offsets, off_row_src, off_slot_pos, off_block_base, total;
+    size_t off_offsets, off_row_src, off_slot_pos, off_block_base, off_tiles, off_tile_expert,
+        total;
     int blocks;
 };
 
@@ -70,6 +71,10 @@ bool route_layout(int32_t T, int32_t E, int32_t k, Layout *L) {
     o += align256(sizeof(int32_t) * (A ? A : 1));
     L->off_block_base = o;
     o += align256(sizeof(int32_t) * (bb ? bb : 1));
+    L->off_tiles = o;
+    o += align256(sizeof(int32_t) * ((size_t)E + 1));
+    L->off_tile_expert = o;  // m-tiles: at most ceil(A / kTileRows) + E
+    o += align256(sizeof(int32_t) * ((A + kTileRows - 1) / kTileRows + (size_t)E));
     L->total = o;
     return true;
 }
@@ -77,7 +82,7 @@ bool route_layout(int32_t T, int32_t E, int32_t k, Layout *L) {
 moeq_status check_route(const moeq_route *r) {
     if (!r) return fail(MOEQ_EINVAL, "route is NULL");
     if (r->magic != kRouteMagic || !r->expert_offsets || !r->row_src || !r->slot_pos ||
-        !r->block_base)
+        !r->block_base || !r->tile_offsets || !r->tile_expert)
         return fail(MOEQ_EINVAL, "route was not bound by moeq_route_bind");
     Layout L;
     if (!route_layout(r->T, r->E, r->top_k, &L) || L.blocks != r->token_blocks)
@@ -205,6 +210,8 @@ moeq_status moeq_route_bind(moeq_route *route, void *workspace, size_t bytes, in
     route->row_src = reinterpret_cast<int32_t *>(base + L.off_row_src);
     route->slot_pos = reinterpret_cast<int32_t *>(base + L.off_slot_pos);
     route->block_base = reinterpret_cast<int32_t *>(base + L.off_block_base);
+    route->tile_offsets = reinterpret_cast<int32_t *>(base + L.off_tiles);
+    route->tile_expert = reinterpret_cast<int32_t *>(base + L.off_tile_expert);
     route->magic = kRouteMagic;
     return MOEQ_OK;
 }
@@ -311,6 +318,8 @@ moeq_status awq_grouped_swiglu(const moeq_route *route, const void *values, moeq
     p.in = values;
     p.out = h;
     p.offsets = route->expert_offsets;
+    p.tile_offsets = route->tile_offsets;
+    p.tile_expert = route->tile_expert;
     p.rows = A;
     p.E = route->E;
     p.act = act;
@@ -343,6 +352,8 @@ moeq_status awq_grouped_down(const moeq_route *route, const void *h, moeq_dtype 
     p.in = h;
     p.out = y;
     p.offsets = route->expert_offsets;
+    p.tile_offsets = route->tile_offsets;
+    p.tile_expert = route->tile_expert;
     p.rows = A;
     p.E = route->E;
     p.act = act;

@@ -58,7 +58,7 @@ __device__ __forceinline__ float e2m1_value(unsigned nib) {
 
 // E8M0 shared scale 2^(byte - 127) (byte 255 is not generated; treated as 2^128).
 __device__ __forceinline__ float e8m0_value(unsigned byte) {
-    return __builtin_ldexpf(1.0f, (int)byte - 127);
+    return byte == 255u ? __builtin_nanf("") : __builtin_ldexpf(1.0f, (int)byte - 127);
 }
 
 // ---------------------------------------------------------------- waves

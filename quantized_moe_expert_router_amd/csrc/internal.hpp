@@ -12,6 +12,7 @@ constexpr uint32_t kRouteMagic = 0x6d6f6571u;  // "moeq"
 constexpr int kTokenBlock = 256;              // tokens per block of the stable scatter
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 2048;
+constexpr int kTileRows = 128;                // rows per m-tile of the tiled projections
 
 // One packed projection operand as the kernels see it (validated on the host).
 struct PackedOperand {
@@ -32,6 +33,8 @@ struct ProjProblem {
     const void *in;
     void *out;
     const int32_t *offsets;
+    const int32_t *tile_offsets;  // [E+1] m-tile prefix (route), nullable
+    const int32_t *tile_expert;   // expert of each m-tile (route), nullable
     int rows;            // total rows (A)
     int E;               // experts in the grid
     int act;             // activation / gradient storage

@@ -147,7 +147,8 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
     const float *__restrict__ bias, int T, int E, int k, uint8_t *__restrict__ values,
     float *__restrict__ weights, uint32_t *__restrict__ selected,
     uint32_t *__restrict__ row_experts, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ row_src_g, int32_t *__restrict__ slot_pos_g) {
+    int32_t *__restrict__ row_src_g, int32_t *__restrict__ slot_pos_g,
+    int32_t *__restrict__ tile_offsets_g, int32_t *__restrict__ tile_expert_g) {
     __shared__ uint16_t sel_s[kSmallA];
     __shared__ float w_s[kSmallA];
     __shared__ int32_t rsrc_s[kSmallA];
@@ -199,6 +200,26 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
         for (int w = 0; w < wv; ++w) base += wave_tot[w];
         if (tid < E) off_s[tid] = base + incl - v;
         if (tid == 0) off_s[E] = A;
+        // m-tile prefix (tiled projections), written by block 0
+        __syncthreads();
+        const int nt = (v + kTileRows - 1) / kTileRows;
+        int tincl = nt;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int n = __shfl_up(tincl, o);
+            if (lane >= o) tincl += n;
+        }
+        if (lane == kWave - 1) wave_tot[wv] = tincl;
+        __syncthreads();
+        int tbase = 0;
+        for (int w = 0; w < wv; ++w) tbase += wave_tot[w];
+        if (blockIdx.x == 0) {
+            if (tid < E) {
+                tile_offsets_g[tid] = tbase + tincl - nt;
+                for (int t = 0; t < nt; ++t) tile_expert_g[tbase + tincl - nt + t] = tid;
+            }
+            if (tid == E - 1) tile_offsets_g[E] = tbase + tincl;
+        }
     }
     __syncthreads();
     // 4. stable positions: rank of token t among the tokens of expert e
@@ -271,7 +292,8 @@ hipError_t launch_dispatch_small(const void *x, size_t row_bytes, const float *l
         hipLaunchKernelGGL(dispatch_small_kernel<N>, dim3(blocks), dim3(1024), 0, s,          \
                            (const uint8_t *)x, (int)row_bytes, logits, bias, T, E, k,           \
                            (uint8_t *)values, weights, selected, row_experts,                  \
-                           route->expert_offsets, route->row_src, route->slot_pos);            \
+                           route->expert_offsets, route->row_src, route->slot_pos,             \
+                           route->tile_offsets, route->tile_expert);                           \
         return hipGetLastError();                                                              \
     }
     MOEQ_SMALL(2)
@@ -330,7 +352,9 @@ __device__ int block_exclusive_scan_1024(int v, int *wave_tot) {
 
 __global__ __launch_bounds__(1024) void block_scan_kernel(int32_t *__restrict__ block_base,
                                                           int nblocks, int E, int A,
-                                                          int32_t *__restrict__ offsets) {
+                                                          int32_t *__restrict__ offsets,
+                                                          int32_t *__restrict__ tile_offsets,
+                                                          int32_t *__restrict__ tile_expert) {
     __shared__ int wave_tot[16];
     // each thread owns experts 2*tid, 2*tid+1 (E <= 2048)
     int tot[2] = {0, 0};
@@ -356,6 +380,19 @@ __global__ __launch_bounds__(1024) void block_scan_kernel(int32_t *__restrict__ 
         }
     }
     if (threadIdx.x == 0) offsets[E] = A;
+    // m-tiles of kTileRows rows per expert, as a prefix over experts
+    __syncthreads();
+    const int nt0 = (tot[0] + kTileRows - 1) / kTileRows, nt1 = (tot[1] + kTileRows - 1) / kTileRows;
+    const int texcl = block_exclusive_scan_1024(nt0 + nt1, wave_tot);
+    for (int q = 0; q < 2; ++q) {
+        const int e = 2 * (int)threadIdx.x + q;
+        const int first = q == 0 ? texcl : texcl + nt0, n = q == 0 ? nt0 : nt1;
+        if (e < E) {
+            tile_offsets[e] = first;
+            for (int t = 0; t < n; ++t) tile_expert[first + t] = e;
+        }
+        if (e == E - 1) tile_offsets[E] = first + n;
+    }
 }
 
 __global__ __launch_bounds__(64) void block_scatter_kernel(
@@ -412,7 +449,7 @@ hipError_t launch_dispatch_index(const uint32_t *selected, int T, int E, int k,
     hipLaunchKernelGGL(block_hist_kernel, dim3(nb), dim3(256), sizeof(int) * E, s, selected,
                        T, k, E, route->block_base);
     hipLaunchKernelGGL(block_scan_kernel, dim3(1), dim3(1024), 0, s, route->block_base, nb, E,
-                       T * k, route->expert_offsets);
+                       T * k, route->expert_offsets, route->tile_offsets, route->tile_expert);
     hipLaunchKernelGGL(block_scatter_kernel, dim3(nb), dim3(64),
                        (sizeof(unsigned long long) + sizeof(int)) * E, s, selected, T, k, E,
                        route->block_base, route->slot_pos, route->row_src, row_experts);

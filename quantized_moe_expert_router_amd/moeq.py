@@ -42,6 +42,7 @@ class Route(C.Structure):
                 ("token_blocks", C.c_int32), ("workspace", C.c_void_p),
                 ("workspace_bytes", C.c_size_t), ("expert_offsets", C.c_void_p),
                 ("row_src", C.c_void_p), ("slot_pos", C.c_void_p), ("block_base", C.c_void_p),
+                ("tile_offsets", C.c_void_p), ("tile_expert", C.c_void_p),
                 ("magic", C.c_uint32)]
 
 

@@ -64,7 +64,8 @@ def test_route_layout(L):
     assert st == moeq.OK and r.T == 300 and r.E == 128 and r.top_k == 8
     n = L.moeq_route_workspace_bytes(300, 128, 8)
     spans = sorted([(r.expert_offsets, 4 * 129), (r.row_src, 4 * 2400), (r.slot_pos, 4 * 2400),
-                    (r.block_base, 4 * 2 * 128)])
+                    (r.block_base, 4 * 2 * 128), (r.tile_offsets, 4 * 129),
+                    (r.tile_expert, 4 * (19 + 128))])
     for (a, la), (b, _) in zip(spans, spans[1:]):
         assert a + la <= b                           # disjoint
     assert spans[0][0] >= FAKE and spans[-1][0] + spans[-1][1] <= FAKE + n

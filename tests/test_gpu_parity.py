@@ -221,3 +221,56 @@ def test_skewed_routing_heavy_experts(sdt, bias):
     tol = TOL["bf16"]
     assert row_rel_err(f64(g["h"], "bf16"), f64(ref["h"], "bf16")) <= tol
     assert row_rel_err(f64(g["out"], "bf16"), f64(ref["out"], "bf16")) <= tol
+
+
+@pytest.mark.parametrize("T,E,k,H,I,sdt,bias", [(200, 8, 2, 512, 256, "bf16", False),
+                                                 (333, 16, 4, 256, 512, "f16", True),
+                                                 (150, 4, 3, 384, 128, "f32", True)])
+def test_tiled_path_parity(T, E, k, H, I, sdt, bias):
+    """Many rows per expert (the LDS-tiled MFMA kernel): several 128-row m-tiles
+    per expert with ragged ends, every stage against the oracle."""
+    cfg = dataclasses.replace(CONFIGS["decode"], T=T, E=E, k=k, H=H, I=I, sdt=sdt,
+                              awq_bias=bias)
+    p = make_inputs(cfg, seed=T + E)
+    print(f"[tile] T={T} E={E} k={k} H={H} I={I} sdt={sdt} bias={bias}", flush=True)
+    g = run_path(p)
+    check_dispatch(p, g)
+    ref = oracle.moe_forward(p)
+    tol = TOL["bf16"]
+    assert row_rel_err(f64(g["h"], "bf16"), f64(ref["h"], "bf16")) <= tol
+    h_or = di.tensor(ref["h"], "bf16", DEV)
+    y_gpu = di.to_host(moeq.awq_grouped_down(g["route"], h_or, g["dev"]["down"]), "bf16")
+    assert row_rel_err(f64(y_gpu, "bf16"), f64(ref["y"], "bf16")) <= tol
+    assert row_rel_err(f64(g["out"], "bf16"), f64(ref["out"], "bf16")) <= tol
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("T,E,k,H,I,edge_scales", [(400, 4, 2, 320, 224, False),
+                                                   (150, 6, 3, 288, 160, False),
+                                                   (90, 3, 2, 256, 128, True)])
+def test_mxfp4_tiled_path_parity(T, E, k, H, I, edge_scales):
+    """MXFP4 bank on the LDS-tiled MFMA kernel: bank row counts that leave a
+    partial 256-row n-tile, several 128-row m-tiles per expert with ragged
+    ends; optionally E8M0 bytes 0 (2^-127) and 255 (NaN) in the scales."""
+    cfg = dataclasses.replace(CONFIGS["mxfp4"], T=T, E=E, k=k, H=H, I=I)
+    p = make_inputs(cfg, seed=7 * T + E)
+    if edge_scales:
+        p["gu_scales"][0, 5, 1] = 0
+        p["gu_scales"][1, 2 * I - 1, 0] = 255
+        p["dn_scales"][2, 0, 0] = 0
+    print(f"[mxfp4 tile] T={T} E={E} k={k} H={H} I={I} edge={edge_scales}", flush=True)
+    g = run_path(p)
+    check_dispatch(p, g)
+    ref = oracle.moe_forward(p)
+    hg, hr = f64(g["h"], "bf16"), f64(ref["h"], "bf16")
+    # NaN must land exactly where the oracle puts it; the rest meets the tolerance
+    assert np.array_equal(np.isnan(hg), np.isnan(hr))
+    keep = ~np.isnan(hr).any(axis=1)
+    assert row_rel_err(hg[keep], hr[keep]) <= TOL["bf16"]
+    h_or = di.tensor(ref["h"], "bf16", DEV)
+    y_gpu = f64(di.to_host(moeq.awq_grouped_down(g["route"], h_or, g["dev"]["down"]), "bf16"),
+                "bf16")
+    yr = f64(ref["y"], "bf16")
+    assert np.array_equal(np.isnan(y_gpu), np.isnan(yr))
+    keep = ~np.isnan(yr).any(axis=1)
+    assert row_rel_err(y_gpu[keep], yr[keep]) <= TOL["bf16"]
