@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (5 launches): the "
+                         "known-size reference that scales the HBM byte counters")
     return ap.parse_args()
 
 
@@ -88,6 +91,55 @@ def flops(p):
     return 6 * A * p["H"] * p["I"]
 
 
+TRAFFIC_SOURCES = ("quantized_moe_expert_router_amd/csrc/gemm_mfma.hip",
+                   "quantized_moe_expert_router_amd/csrc/awq_dequant.hpp",
+                   "quantized_moe_expert_router_amd/csrc/common.hpp",
+                   "quantized_moe_expert_router_amd/csrc/internal.hpp")
+
+
+def kernel_digest():
+    """Digest of the sources the gate/up stream kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config_name):
+    """HBM bytes per launch of the gate/up kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's counters), or
+    None when there is none for this workload or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", f"awq_stream_kernel.{config_name}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                vals[key.strip()] = val.strip()
+    if vals.get("source_digest") != kernel_digest():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(mib):
+    """A plain device-to-device copy of known size, launched 5 times."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+
+
 def cpu_baseline(cfg, target_s):
     """The oracle as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -117,6 +169,10 @@ def main():
               "shards by tokens or by expert ranges, but this build runs on one GPU)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
 
     import numpy as np
     import torch
@@ -218,6 +274,7 @@ def main():
     F = flops(p)
     tok_s = T / (ms * 1e-3)
     achieved = ab["gateup"] / (k_ms * 1e-3) / 1e9
+    traffic = measured_traffic(cfg.name)
     path_gbs = ab["total"] / (ms * 1e-3) / 1e9
     path_tflops = F / (ms * 1e-3) / 1e12
     res = {
@@ -231,7 +288,7 @@ def main():
         "roofline": {"kernel": "awq_grouped_swiglu (gate/up dequant-GEMM + SwiGLU)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel_ms": round(k_ms, 5),
+                     "traffic": traffic, "kernel_ms": round(k_ms, 5),
                      "alg_bytes_per_launch": ab["gateup"]},
         "path": {"alg_bytes": ab["total"], "alg_flops": F, "GBs": round(path_gbs, 1),
                  "hbm_frac": round(path_gbs / HBM_PEAK_GBS, 4),
