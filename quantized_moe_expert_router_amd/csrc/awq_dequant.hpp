@@ -63,13 +63,27 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});  // v_cvt_pk_bf16_f32
 }
 
+// SwiGLU for bf16 outputs: the hardware exp and reciprocal (about one fp32 ulp
+// each) stay far inside the bf16 rounding of h.
 __device__ __forceinline__ float swiglu_f(float g, float u, float clamp, float alpha, float off) {
     if (clamp > 0.0f) {
         g = fminf(fmaxf(g, -clamp), clamp);
         u = fminf(fmaxf(u, -clamp), clamp);
     }
-    return g * (1.0f / (1.0f + expf(-alpha * g))) * (u + off);
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-alpha * g)) * (u + off);
 }
+
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
+// only.  __syncthreads() also waits for every global load in flight
+// (vmcnt(0)), which would drain the prefetch ring at each barrier.  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Barrier that only aligns the waves of a block (no memory hand-off): nothing
+// in flight is waited for.
+__device__ __forceinline__ void lockstep_barrier() { __builtin_amdgcn_s_barrier(); }
 
 constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 buffer descriptor, 32-bit data
 

@@ -28,6 +28,8 @@ namespace moeq {
 bool tile_fits(const ProjProblem &p);
 hipError_t launch_tile(const ProjProblem &p, const int32_t *tile_offsets,
                        const int32_t *tile_expert, hipStream_t s);
+bool wave_fits(const ProjProblem &p);
+hipError_t launch_wave(const ProjProblem &p, hipStream_t s);
 
 namespace {
 
@@ -206,7 +208,7 @@ void awq_stream_kernel(StreamArgs a) {
                 issue_rows(d, kbeg + 32 * d);
             }
             for (int gi = gbeg; gi < gend; ++gi) {
-                __syncthreads();  // lockstep: the block reads one row block at a time
+                lockstep_barrier();  // the block reads one row block at a time
                 decode_group<SD>(graw, gc);
 #pragma unroll
                 for (int t = 0; t < SPG; ++t) {
@@ -237,7 +239,7 @@ void awq_stream_kernel(StreamArgs a) {
                     bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, voff_a[rt], kbeg * 2, 0));
             int it = 0;
             for (int k0 = kbeg; k0 < kend; k0 += 32, ++it) {
-                if ((it & 3) == 0) __syncthreads();
+                if ((it & 3) == 0) lockstep_barrier();
                 if (k0 == kbeg || k0 % g == 0) decode_group<SD>(graw, gc);
                 const int kn = k0 + 32;
                 if (kn < kend) {
@@ -446,6 +448,10 @@ hipError_t launch_fast_swiglu(const ProjProblem &p, hipStream_t s, bool *handled
         *handled = true;
         return run_stream<2>(p, s);
     }
+    if (wave_fits(p)) {
+        *handled = true;
+        return launch_wave(p, s);
+    }
     if (p.tile_offsets && tile_fits(p)) {
         *handled = true;
         return launch_tile(p, p.tile_offsets, p.tile_expert, s);
@@ -459,6 +465,10 @@ hipError_t launch_fast_plain(const ProjProblem &p, hipStream_t s, bool *handled)
     if (stream_fits(p)) {
         *handled = true;
         return run_stream<1>(p, s);
+    }
+    if (wave_fits(p)) {
+        *handled = true;
+        return launch_wave(p, s);
     }
     if (p.tile_offsets && tile_fits(p)) {
         *handled = true;

@@ -243,17 +243,17 @@ __global__ __launch_bounds__(256, 2) void awq_tile_kernel(TileArgs a) {
     load_step(st[1], 1);
     store_step(st[0], 0, 0);
     load_step(st[0], 2);
-    __syncthreads();
+    lds_barrier();
     for (int ks = 0; ks < nsteps; ks += 2) {
         mfma_step(0);
         if (ks + 1 < nsteps) store_step(st[1], ks + 1, 1);
         load_step(st[1], ks + 3);
-        __syncthreads();
+        lds_barrier();
         if (ks + 1 >= nsteps) break;
         mfma_step(1);
         if (ks + 2 < nsteps) store_step(st[0], ks + 2, 0);
         load_step(st[0], ks + 4);
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- epilogue: bias, storage rounding, SwiGLU; LDS column -> output column

@@ -226,13 +226,17 @@ def test_skewed_routing_heavy_experts(sdt, bias):
 @pytest.mark.parametrize("T,E,k,H,I,sdt,bias", [(200, 8, 2, 512, 256, "bf16", False),
                                                  (333, 16, 4, 256, 512, "f16", True),
                                                  (150, 4, 3, 384, 128, "f32", True)])
-def test_tiled_path_parity(T, E, k, H, I, sdt, bias):
-    """Many rows per expert (the LDS-tiled MFMA kernel): several 128-row m-tiles
-    per expert with ragged ends, every stage against the oracle."""
+@pytest.mark.parametrize("kernel", ["wave", "tile"])
+def test_tiled_path_parity(T, E, k, H, I, sdt, bias, kernel, monkeypatch):
+    """Many rows per expert: several 128-row m-tiles per expert with ragged
+    ends, every stage against the oracle, on the register-decoded wave kernel
+    and (with it switched off) on the LDS-tiled kernel."""
+    if kernel == "tile":
+        monkeypatch.setenv("MOEQ_WAVE", "0")
     cfg = dataclasses.replace(CONFIGS["decode"], T=T, E=E, k=k, H=H, I=I, sdt=sdt,
                               awq_bias=bias)
     p = make_inputs(cfg, seed=T + E)
-    print(f"[tile] T={T} E={E} k={k} H={H} I={I} sdt={sdt} bias={bias}", flush=True)
+    print(f"[{kernel}] T={T} E={E} k={k} H={H} I={I} sdt={sdt} bias={bias}", flush=True)
     g = run_path(p)
     check_dispatch(p, g)
     ref = oracle.moe_forward(p)
