@@ -30,6 +30,8 @@ hipError_t launch_tile(const ProjProblem &p, const int32_t *tile_offsets,
                        const int32_t *tile_expert, hipStream_t s);
 bool wave_fits(const ProjProblem &p);
 hipError_t launch_wave(const ProjProblem &p, hipStream_t s);
+bool mx_fits(const ProjProblem &p);
+hipError_t launch_mx(const ProjProblem &p, hipStream_t s);
 
 namespace {
 
@@ -437,6 +439,10 @@ hipError_t run_stream(const ProjProblem &p, hipStream_t s) {
 hipError_t launch_fast_swiglu(const ProjProblem &p, hipStream_t s, bool *handled) {
     *handled = false;
     if (p.mode == PROJ_BANK_SWIGLU) {
+        if (mx_fits(p)) {
+            *handled = true;
+            return launch_mx(p, s);
+        }
         if (p.tile_offsets && tile_fits(p)) {
             *handled = true;
             return launch_tile(p, p.tile_offsets, p.tile_expert, s);
@@ -462,6 +468,10 @@ hipError_t launch_fast_swiglu(const ProjProblem &p, hipStream_t s, bool *handled
 hipError_t launch_fast_plain(const ProjProblem &p, hipStream_t s, bool *handled) {
     *handled = false;
     if (p.mode != PROJ_PLAIN) return hipSuccess;
+    if (mx_fits(p)) {
+        *handled = true;
+        return launch_mx(p, s);
+    }
     if (stream_fits(p)) {
         *handled = true;
         return run_stream<1>(p, s);

@@ -42,7 +42,12 @@ using namespace awq;
 constexpr int kBM = kTileRows;   // 128 rows per block tile
 constexpr int kUnits = 32;       // word-column units per block tile (x 8 columns)
 constexpr int kBCols = kUnits * 8;
-constexpr int kLdsRow = 40;      // bf16 per LDS row: 32 k + 8 pad (80 bytes)
+constexpr int kLdsRow = 32;  // LDS row: 32 bf16 (one K step), 16-byte chunks permuted
+
+// 16-byte chunk position of chunk ch of LDS row `row`: measured on gfx950,
+// chunk ^ ((row >> 1) & 3) lets the MFMA fragment reads (16 rows x one chunk
+// per 16 lanes) run at the full 256 bytes per clock.
+__device__ __forceinline__ int lds_chunk(int row, int ch) { return ch ^ ((row >> 1) & 3); }
 
 struct TileArgs {
     const __bf16 *in;             // [A, K] rows sorted by expert
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(256, 2) void awq_tile_kernel(TileArgs a) {
     auto store_step = [&](const Stage &S, int ks, int buf) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            *reinterpret_cast<u32x4 *>(&As[buf][arow[h]][8 * apart[h]]) = S.ar[h];
+            *reinterpret_cast<u32x4 *>(&As[buf][arow[h]][8 * lds_chunk(arow[h], apart[h])]) = S.ar[h];
         if constexpr (MX) {
             // E8M0 scale 2^(s-127) as fp32: s = 0 is the subnormal 2^-127, s = 255 NaN
             const uint32_t sbits = S.sbyte == 255u ? 0x7FC00000u
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void awq_tile_kernel(TileArgs a) {
                 v[1] = __builtin_bit_cast(uint32_t, p1);
                 v[2] = __builtin_bit_cast(uint32_t, p2);
                 v[3] = __builtin_bit_cast(uint32_t, p3);
-                *reinterpret_cast<u32x4 *>(&Bs[buf][mxcol][8 * d]) = v;
+                *reinterpret_cast<u32x4 *>(&Bs[buf][mxcol][8 * lds_chunk(mxcol, d)]) = v;
             }
         } else {
             if ((ks * 32) % g == 0) decode_group<SD>(S.graw, gc);
@@ -192,7 +197,8 @@ __global__ __launch_bounds__(256, 2) void awq_tile_kernel(TileArgs a) {
                 uint2 v;
                 v.x = pack_bf16(coeff<SD>(q[0][sl], gc, sl), coeff<SD>(q[1][sl], gc, sl));
                 v.y = pack_bf16(coeff<SD>(q[2][sl], gc, sl), coeff<SD>(q[3][sl], gc, sl));
-                *reinterpret_cast<uint2 *>(&Bs[buf][kSlotCol[sl] * kUnits + u][4 * kq]) = v;
+                const int L = kSlotCol[sl] * kUnits + u;
+                *reinterpret_cast<uint2 *>(&Bs[buf][L][8 * lds_chunk(L, kq >> 1) + 4 * (kq & 1)]) = v;
             }
         }
     };
@@ -223,10 +229,12 @@ __global__ __launch_bounds__(256, 2) void awq_tile_kernel(TileArgs a) {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
             if (rt < rtn)
-                af[rt] = *reinterpret_cast<const bf16x8 *>(&As[buf][wm * 64 + rt * 16 + c][grp * 8]);
+                af[rt] = *reinterpret_cast<const bf16x8 *>(
+                    &As[buf][wm * 64 + rt * 16 + c][8 * lds_chunk(c, grp)]);
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
-            const bf16x8 bf = *reinterpret_cast<const bf16x8 *>(&Bs[buf][bcol(ct) + c][grp * 8]);
+            const bf16x8 bf =
+                *reinterpret_cast<const bf16x8 *>(&Bs[buf][bcol(ct) + c][8 * lds_chunk(c, grp)]);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
                 if (rt < rtn)

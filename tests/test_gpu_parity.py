@@ -249,20 +249,25 @@ def test_tiled_path_parity(T, E, k, H, I, sdt, bias, kernel, monkeypatch):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("kernel", ["mx", "tile"])
 @pytest.mark.parametrize("T,E,k,H,I,edge_scales", [(400, 4, 2, 320, 224, False),
                                                    (150, 6, 3, 288, 160, False),
-                                                   (90, 3, 2, 256, 128, True)])
-def test_mxfp4_tiled_path_parity(T, E, k, H, I, edge_scales):
-    """MXFP4 bank on the LDS-tiled MFMA kernel: bank row counts that leave a
-    partial 256-row n-tile, several 128-row m-tiles per expert with ragged
-    ends; optionally E8M0 bytes 0 (2^-127) and 255 (NaN) in the scales."""
+                                                   (90, 3, 2, 256, 128, True),
+                                                   (20, 4, 1, 256, 64, False)])
+def test_mxfp4_tiled_path_parity(T, E, k, H, I, edge_scales, kernel, monkeypatch):
+    """MXFP4 bank on the register-decoded kernel and (switched off) on the
+    LDS-tiled kernel: bank row counts that leave partial column tiles, K not a
+    multiple of 128, 2 to 8 live row tiles, several 128-row m-tiles per expert
+    with ragged ends; optionally E8M0 bytes 0 (2^-127) and 255 (NaN)."""
+    if kernel == "tile":
+        monkeypatch.setenv("MOEQ_MX", "0")
     cfg = dataclasses.replace(CONFIGS["mxfp4"], T=T, E=E, k=k, H=H, I=I)
     p = make_inputs(cfg, seed=7 * T + E)
     if edge_scales:
         p["gu_scales"][0, 5, 1] = 0
         p["gu_scales"][1, 2 * I - 1, 0] = 255
         p["dn_scales"][2, 0, 0] = 0
-    print(f"[mxfp4 tile] T={T} E={E} k={k} H={H} I={I} edge={edge_scales}", flush=True)
+    print(f"[mxfp4 {kernel}] T={T} E={E} k={k} H={H} I={I} edge={edge_scales}", flush=True)
     g = run_path(p)
     check_dispatch(p, g)
     ref = oracle.moe_forward(p)
