@@ -73,11 +73,16 @@ __global__ __launch_bounds__(256, 2) void awq_tile_kernel(TileArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 As[2][kBM][kLdsRow];
     __shared__ __attribute__((aligned(16))) __bf16 Bs[2][kBCols][kLdsRow];
 
-    // ---- which tile: the n-tiles of an m-tile share an XCD (block b runs on
-    // XCD b % 8): b = 8 * (ntiles * n + nt) + x holds m-tile 8n + x, n-tile nt
+    // ---- which tile: the m-tiles are split into eight contiguous ranges, one
+    // per XCD (block b runs on XCD b % 8), so consecutive m-tiles of an expert
+    // reuse its weights from that XCD's L2; the n-tiles of an m-tile run there
+    // back to back and share its rows
+    const int mtiles = a.tile_offsets[a.E];
+    const int per_xcd = (mtiles + 7) / 8;
     const int x = blockIdx.x % 8, idx = blockIdx.x / 8;
-    const int mt = (idx / a.ntiles) * 8 + x, nt = idx % a.ntiles;
-    if (mt >= a.tile_offsets[a.E]) return;
+    const int local = idx / a.ntiles, nt = idx % a.ntiles;
+    const int mt = x * per_xcd + local;
+    if (local >= per_xcd || mt >= mtiles) return;
     const int e = a.tile_expert[mt];
     const int r_end = a.offsets[e + 1];
     const int m0 = a.offsets[e] + (mt - a.tile_offsets[e]) * kBM;
