@@ -6,7 +6,8 @@ softmax + stable COPY dispatch) -> awq_grouped_swiglu -> awq_grouped_down ->
 moe_combine.  Inputs are seeded synthetic tensors resident in HBM before the
 timed region.  Each step reads a different replica of the expert weights (as
 consecutive MoE layers would), so no step finds the previous step's weights in
-the 256 MB last-level cache.  Steps are captured once as HIP graphs and replayed.
+the 256 MB last-level cache.  Steps are captured once as HIP graphs -- a whole
+cycle over the replicas in one graph -- and replayed.
 
 Prints ONE JSON line.  Default workload: the decode-shaped AWQ MoE
 (T=64, hidden 2048, intermediate 768, 128 experts, top_k 8, group 128, bf16).
@@ -231,26 +232,37 @@ def main():
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
 
-    graphs = None
+    graphs = cycle = None
     if not args.eager:
+        # one graph per replica, and one holding a whole cycle of R steps (the
+        # way consecutive MoE layers of a model would be captured together)
         graphs = []
         for r in range(R):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 step(r)
             graphs.append(g)
+        cycle = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cycle):
+            for r in range(R):
+                step(r)
         for i in range(args.warmup):
             graphs[i % R].replay()
+        cycle.replay()
         torch.cuda.synchronize()
 
     # ---- timed region: exactly `steps` steps
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
-    for i in range(args.steps):
-        if graphs is not None:
-            graphs[i % R].replay()
-        else:
+    if graphs is not None:
+        full, rest = divmod(args.steps, R)
+        for _ in range(full):
+            cycle.replay()
+        for i in range(rest):
+            graphs[i].replay()
+    else:
+        for i in range(args.steps):
             step(i)
     ev1.record()
     torch.cuda.synchronize()
