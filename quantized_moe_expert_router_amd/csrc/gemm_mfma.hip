@@ -30,6 +30,8 @@ hipError_t launch_tile(const ProjProblem &p, const int32_t *tile_offsets,
                        const int32_t *tile_expert, hipStream_t s);
 bool wave_fits(const ProjProblem &p);
 hipError_t launch_wave(const ProjProblem &p, hipStream_t s);
+bool ws_fits(const ProjProblem &p);
+hipError_t launch_ws(const ProjProblem &p, hipStream_t s);
 bool mx_fits(const ProjProblem &p);
 hipError_t launch_mx(const ProjProblem &p, hipStream_t s);
 
@@ -435,7 +437,8 @@ hipError_t run_stream(const ProjProblem &p, hipStream_t s) {
 
 }  // namespace
 
-// Few rows per expert: the weight-streaming kernel; many: the LDS-tiled one.
+// Few rows per expert: the weight-streaming kernel; many: the register-decoded
+// wave kernel, then the warp-specialised one (fp32 scales), then the LDS-tiled one.
 hipError_t launch_fast_swiglu(const ProjProblem &p, hipStream_t s, bool *handled) {
     *handled = false;
     if (p.mode == PROJ_BANK_SWIGLU) {
@@ -458,6 +461,10 @@ hipError_t launch_fast_swiglu(const ProjProblem &p, hipStream_t s, bool *handled
         *handled = true;
         return launch_wave(p, s);
     }
+    if (ws_fits(p)) {
+        *handled = true;
+        return launch_ws(p, s);
+    }
     if (p.tile_offsets && tile_fits(p)) {
         *handled = true;
         return launch_tile(p, p.tile_offsets, p.tile_expert, s);
@@ -479,6 +486,10 @@ hipError_t launch_fast_plain(const ProjProblem &p, hipStream_t s, bool *handled)
     if (wave_fits(p)) {
         *handled = true;
         return launch_wave(p, s);
+    }
+    if (ws_fits(p)) {
+        *handled = true;
+        return launch_ws(p, s);
     }
     if (p.tile_offsets && tile_fits(p)) {
         *handled = true;

@@ -226,13 +226,16 @@ def test_skewed_routing_heavy_experts(sdt, bias):
 @pytest.mark.parametrize("T,E,k,H,I,sdt,bias", [(200, 8, 2, 512, 256, "bf16", False),
                                                  (333, 16, 4, 256, 512, "f16", True),
                                                  (150, 4, 3, 384, 128, "f32", True)])
-@pytest.mark.parametrize("kernel", ["wave", "tile"])
+@pytest.mark.parametrize("kernel", ["ws", "wave", "tile"])
 def test_tiled_path_parity(T, E, k, H, I, sdt, bias, kernel, monkeypatch):
     """Many rows per expert: several 128-row m-tiles per expert with ragged
-    ends, every stage against the oracle, on the register-decoded wave kernel
-    and (with it switched off) on the LDS-tiled kernel."""
-    if kernel == "tile":
+    ends, every stage against the oracle, on each of the register-decoded wave
+    kernel (bf16 and fp16 scales), the warp-specialised kernel and the
+    LDS-tiled kernel, the others switched off."""
+    if kernel in ("ws", "tile"):
         monkeypatch.setenv("MOEQ_WAVE", "0")
+    if kernel in ("wave", "tile"):
+        monkeypatch.setenv("MOEQ_WS", "0")
     cfg = dataclasses.replace(CONFIGS["decode"], T=T, E=E, k=k, H=H, I=I, sdt=sdt,
                               awq_bias=bias)
     p = make_inputs(cfg, seed=T + E)
