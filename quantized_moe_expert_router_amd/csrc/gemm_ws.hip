@@ -186,9 +186,15 @@ void awq_ws_kernel(WsArgs a) {
         using I1 = std::integral_constant<int, 1>;
         using I2 = std::integral_constant<int, 2>;
 
+        // the scheduler must not sink these loads past the first refill: the
+        // compiler's wait counts on the loop entry would then assume slot 2
+        // was loaded last and wait for it on every trip
         issue(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
         issue(1, 1);
+        __builtin_amdgcn_sched_barrier(0);
         issue(2, 2);
+        __builtin_amdgcn_sched_barrier(0);
         // step q is produced in iteration q - 1 (step 0 before the loop); the
         // consumers run step q in iteration q.  Steps past the end decode
         // clamped data into a buffer nobody reads, keeping every iteration's
