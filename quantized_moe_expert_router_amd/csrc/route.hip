@@ -308,9 +308,8 @@ hipError_t launch_dispatch_small(const void *x, size_t row_bytes, const float *l
 //  1. block_hist: per block of kTokenBlock tokens, the count of each expert.
 //  2. block_scan: expert_offsets = exclusive scan of the totals; block_base[b][e]
 //     = first sorted row of expert e for token block b.
-//  3. block_scatter: one wave walks its block 64 tokens at a time; the rank of
-//     a token among the chunk's tokens that chose the same expert is the
-//     popcount of the lower lanes in that expert's 64-bit chunk mask.
+//  3. block_scatter: the rank of a token among the block's tokens that chose
+//     the same expert is a popcount over per-wave 64-bit token masks.
 __global__ __launch_bounds__(256) void block_hist_kernel(const uint32_t *__restrict__ selected,
                                                          int T, int k, int E,
                                                          int32_t *__restrict__ block_base) {
@@ -356,27 +355,41 @@ __global__ __launch_bounds__(1024) void block_scan_kernel(int32_t *__restrict__ 
                                                           int32_t *__restrict__ tile_offsets,
                                                           int32_t *__restrict__ tile_expert) {
     __shared__ int wave_tot[16];
-    // each thread owns experts 2*tid, 2*tid+1 (E <= 2048)
+    constexpr int kBatch = 8;  // independent loads in flight per thread
+    // each thread owns experts 2*tid, 2*tid+1 (E <= 2048); pass 1: totals
     int tot[2] = {0, 0};
     for (int q = 0; q < 2; ++q) {
         const int e = 2 * (int)threadIdx.x + q;
         if (e < E) {
-            int run = 0;
-            for (int b = 0; b < nblocks; ++b) {
-                const int c = block_base[(size_t)b * E + e];
-                block_base[(size_t)b * E + e] = run;
-                run += c;
+            for (int b0 = 0; b0 < nblocks; b0 += kBatch) {
+                int c[kBatch];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    c[i] = b0 + i < nblocks ? block_base[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i) tot[q] += c[i];
             }
-            tot[q] = run;
         }
     }
     const int excl = block_exclusive_scan_1024(tot[0] + tot[1], wave_tot);
     const int starts[2] = {excl, excl + tot[0]};
+    // pass 2: block_base[b][e] = first sorted row of expert e for token block b
     for (int q = 0; q < 2; ++q) {
         const int e = 2 * (int)threadIdx.x + q;
         if (e < E) {
             offsets[e] = starts[q];
-            for (int b = 0; b < nblocks; ++b) block_base[(size_t)b * E + e] += starts[q];
+            int run = starts[q];
+            for (int b0 = 0; b0 < nblocks; b0 += kBatch) {
+                int c[kBatch];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    c[i] = b0 + i < nblocks ? block_base[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i) {
+                    if (b0 + i < nblocks) block_base[(size_t)(b0 + i) * E + e] = run;
+                    run += c[i];
+                }
+            }
         }
     }
     if (threadIdx.x == 0) offsets[E] = A;
@@ -395,50 +408,36 @@ __global__ __launch_bounds__(1024) void block_scan_kernel(int32_t *__restrict__ 
     }
 }
 
-__global__ __launch_bounds__(64) void block_scatter_kernel(
+// Wave w of the block ranks tokens 64w .. 64w + 63 of the token block: the rank
+// of token t among the block's tokens that chose expert e is the popcount of
+// the chosen-e masks of the earlier waves plus that of the lower lanes of its
+// own wave.  Two barriers per block.
+constexpr int kScatterWaves = kTokenBlock / 64;
+__global__ __launch_bounds__(kTokenBlock) void block_scatter_kernel(
     const uint32_t *__restrict__ selected, int T, int k, int E,
     const int32_t *__restrict__ block_base, int32_t *__restrict__ slot_pos,
     int32_t *__restrict__ row_src, uint32_t *__restrict__ row_experts) {
     extern __shared__ unsigned long long smem_u64[];
-    unsigned long long *mask = smem_u64;              // [E]
-    int *cnt = reinterpret_cast<int *>(mask + E);     // [E]
-    const int b = blockIdx.x, lane = threadIdx.x;
-    for (int e = lane; e < E; e += kWave) {
-        cnt[e] = block_base[(size_t)b * E + e];
-        mask[e] = 0ull;
-    }
+    unsigned long long *mask = smem_u64;  // [kScatterWaves][E]
+    const int b = blockIdx.x, w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    for (int i = threadIdx.x; i < kScatterWaves * E; i += blockDim.x) mask[i] = 0ull;
     __syncthreads();
-    const int t_end = min((b + 1) * kTokenBlock, T);
-    const unsigned long long lower = (1ull << lane) - 1ull;
-    for (int t0 = b * kTokenBlock; t0 < t_end; t0 += kWave) {
-        const int t = t0 + lane;
-        const bool valid = t < t_end;
-        if (valid)
-            for (int j = 0; j < k; ++j) atomicOr(&mask[selected[(size_t)t * k + j]], 1ull << lane);
-        __syncthreads();
-        uint32_t lowest = 0;  // bit j: this lane is the first chunk lane of expert sel[t][j]
-        if (valid)
-            for (int j = 0; j < k; ++j) {
-                const uint32_t e = selected[(size_t)t * k + j];
-                const unsigned long long m = mask[e];
-                const int p = cnt[e] + __popcll(m & lower);
-                slot_pos[(size_t)t * k + j] = p;
-                row_src[p] = t;
-                row_experts[p] = e;
-                if ((m & lower) == 0ull) lowest |= 1u << j;
-            }
-        __syncthreads();
-        if (valid)
-            for (int j = 0; j < k; ++j)
-                if ((lowest >> j) & 1u) {
-                    const uint32_t e = selected[(size_t)t * k + j];
-                    cnt[e] += __popcll(mask[e]);
-                }
-        __syncthreads();
-        if (valid)
-            for (int j = 0; j < k; ++j)
-                if ((lowest >> j) & 1u) mask[selected[(size_t)t * k + j]] = 0ull;
-        __syncthreads();
+    const int t = b * kTokenBlock + (int)threadIdx.x;
+    const bool valid = t < T;
+    if (valid)
+        for (int j = 0; j < k; ++j)
+            atomicOr(&mask[w * E + selected[(size_t)t * k + j]], 1ull << lane);
+    __syncthreads();
+    if (valid) {
+        const unsigned long long lower = (1ull << lane) - 1ull;
+        for (int j = 0; j < k; ++j) {
+            const uint32_t e = selected[(size_t)t * k + j];
+            int p = block_base[(size_t)b * E + e] + __popcll(mask[w * E + e] & lower);
+            for (int v = 0; v < w; ++v) p += __popcll(mask[v * E + e]);
+            slot_pos[(size_t)t * k + j] = p;
+            row_src[p] = t;
+            row_experts[p] = e;
+        }
     }
 }
 
@@ -450,8 +449,8 @@ hipError_t launch_dispatch_index(const uint32_t *selected, int T, int E, int k,
                        T, k, E, route->block_base);
     hipLaunchKernelGGL(block_scan_kernel, dim3(1), dim3(1024), 0, s, route->block_base, nb, E,
                        T * k, route->expert_offsets, route->tile_offsets, route->tile_expert);
-    hipLaunchKernelGGL(block_scatter_kernel, dim3(nb), dim3(64),
-                       (sizeof(unsigned long long) + sizeof(int)) * E, s, selected, T, k, E,
+    hipLaunchKernelGGL(block_scatter_kernel, dim3(nb), dim3(kTokenBlock),
+                       sizeof(unsigned long long) * kScatterWaves * E, s, selected, T, k, E,
                        route->block_base, route->slot_pos, route->row_src, row_experts);
     return hipGetLastError();
 }
