@@ -59,17 +59,22 @@ __device__ __forceinline__ void route_token(const float *__restrict__ logits,
                                             int r, int group_base_lane, int *sel_out,
                                             float *w_out) {
     const float *row = logits + (size_t)t * E;
+    // all loads first (clamped index, no branch), so the lane waits once
+    float v[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] = row[min(r + LANES * i, E - 1)];
+    if (bias) {
+        float b[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) b[i] = bias[min(r + LANES * i, E - 1)];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) v[i] = v[i] + b[i];  // one IEEE fp32 add
+    }
     uint64_t key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = r + LANES * i;
-        if (e < E) {
-            float v = row[e];
-            if (bias) v = v + bias[e];  // one IEEE fp32 add
-            key[i] = sel_key(v, e);
-        } else {
-            key[i] = 0;
-        }
+        key[i] = e < E ? sel_key(v[i], e) : 0;
     }
     uint64_t mine = 0;
     for (int j = 0; j < k; ++j) {
