@@ -500,8 +500,10 @@ hipError_t launch_copy_rows(const void *x, size_t row_bytes, int A, const int32_
 // One block per token.  The k sorted positions are ranked so that slot a of
 // the shared list is the a-th smallest position, i.e. the a-th smallest expert
 // ID; every column then runs acc = fma(w, y, acc) in that order.  Each thread
-// owns VEC consecutive columns and moves them as one 16-byte vector.
-template <int ACT>
+// owns VEC consecutive columns and moves them as one 16-byte vector; its row
+// loads are all issued before the first fma (KM >= k bounds them at compile
+// time).
+template <int ACT, int KM>
 __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y,
                                                       const float *__restrict__ weights,
                                                       const int32_t *__restrict__ slot_pos,
@@ -510,29 +512,42 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
     typedef typename Storage<ACT>::T S;
     constexpr int VEC = 16 / sizeof(S);
     typedef S sv __attribute__((ext_vector_type(VEC)));
-    __shared__ int pos_s[kMaxTopK];
-    __shared__ float w_s[kMaxTopK];
+    __shared__ int raw_s[KM];
+    __shared__ float wraw_s[KM];
+    __shared__ int pos_s[KM];
+    __shared__ float w_s[KM];
     const int t = blockIdx.x;
     if ((int)threadIdx.x < k) {
-        const int p = slot_pos[(size_t)t * k + threadIdx.x];
+        raw_s[threadIdx.x] = slot_pos[(size_t)t * k + threadIdx.x];
+        wraw_s[threadIdx.x] = weights[(size_t)t * k + threadIdx.x];
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < k) {
+        const int p = raw_s[threadIdx.x];
         int rank = 0;
-        for (int j = 0; j < k; ++j) rank += slot_pos[(size_t)t * k + j] < p;
+        for (int j = 0; j < k; ++j) rank += raw_s[j] < p;
         pos_s[rank] = p;
-        w_s[rank] = weights[(size_t)t * k + threadIdx.x];
+        w_s[rank] = wraw_s[threadIdx.x];
     }
     __syncthreads();
     const S *ys = static_cast<const S *>(y);
     S *os = static_cast<S *>(out);
     if (vec_ok) {
         for (int c = threadIdx.x * VEC; c < K; c += blockDim.x * VEC) {
+            sv yv[KM];  // slots past k reload slot k - 1 (no branch around a load)
+#pragma unroll
+            for (int a = 0; a < KM; ++a)
+                yv[a] = *reinterpret_cast<const sv *>(ys + (size_t)pos_s[min(a, k - 1)] * K + c);
             float acc[VEC];
 #pragma unroll
             for (int v = 0; v < VEC; ++v) acc[v] = 0.0f;
-            for (int a = 0; a < k; ++a) {
-                const sv yv = *reinterpret_cast<const sv *>(ys + (size_t)pos_s[a] * K + c);
-                const float w = w_s[a];
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) acc[v] = __builtin_fmaf(w, (float)yv[v], acc[v]);
+            for (int a = 0; a < KM; ++a) {
+                if (a < k) {
+                    const float w = w_s[a];
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) acc[v] = __builtin_fmaf(w, (float)yv[a][v], acc[v]);
+                }
             }
             sv o;
 #pragma unroll
@@ -557,15 +572,23 @@ hipError_t launch_combine(const void *y, int act, const float *weights,
     const bool vec_ok = ((uintptr_t)y | (uintptr_t)out) % 16 == 0 && K % vec == 0;
     int threads = vec_ok ? K / vec : K;
     threads = threads >= 256 ? 256 : ((threads + 63) / 64) * 64;
-#define MOEQ_COMBINE(DT)                                                                   \
-    hipLaunchKernelGGL(combine_kernel<DT>, dim3(T), dim3(threads), 0, s, y, weights, slot_pos, \
-                       T, k, K, vec_ok, out)
+#define MOEQ_COMBINE(DT, KM)                                                               \
+    hipLaunchKernelGGL((combine_kernel<DT, KM>), dim3(T), dim3(threads), 0, s, y, weights,   \
+                       slot_pos, T, k, K, vec_ok, out)
+#define MOEQ_COMBINE_K(DT)            \
+    if (k <= 8)                       \
+        MOEQ_COMBINE(DT, 8);          \
+    else if (k <= 16)                 \
+        MOEQ_COMBINE(DT, 16);         \
+    else                              \
+        MOEQ_COMBINE(DT, kMaxTopK)
     if (act == MOEQ_F32)
-        MOEQ_COMBINE(MOEQ_F32);
+        MOEQ_COMBINE_K(MOEQ_F32);
     else if (act == MOEQ_BF16)
-        MOEQ_COMBINE(MOEQ_BF16);
+        MOEQ_COMBINE_K(MOEQ_BF16);
     else
-        MOEQ_COMBINE(MOEQ_F16);
+        MOEQ_COMBINE_K(MOEQ_F16);
+#undef MOEQ_COMBINE_K
 #undef MOEQ_COMBINE
     return hipGetLastError();
 }
