@@ -164,9 +164,12 @@ void mx_wave_kernel(MxArgs a) {
             float sc[kCT];
 #pragma unroll
             for (int ct = 0; ct < kCT; ++ct) sc[ct] = e8m0_scale(sw[d][ct] & 0xFFu);
-            // next super-step's A tile into the other buffer
+            // next super-step's A tile into the other buffer; the loads stay
+            // in program order (A tile, then the block refill at the end)
             store_a(buf ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
             issue_a(ss + 2);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 // row tiles in groups of at most four: fewer live A fragments
@@ -203,15 +206,26 @@ void mx_wave_kernel(MxArgs a) {
                     else rows(I4{}, I4{});
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
             issue_b(d, ss + DB);  // this slot's blocks are consumed: refill it
+            __builtin_amdgcn_sched_barrier(0);
             lds_barrier();
         };
 
-#pragma unroll
-        for (int d = 0; d < DB; ++d) issue_b(d, d);
+        // Prologue in the loop's own load order -- a step issues the A tile
+        // two super-steps ahead, then refills its block slot -- so that on the
+        // loop entry the next A tile is again followed by one slot's block
+        // loads; scheduling barriers keep the compiler's wait counts exact
+        // (otherwise the first step of every trip drains the whole ring).
+        issue_b(0, 0);
+        issue_b(1, 1);
         issue_a(0);
         store_a(0);
+        __builtin_amdgcn_sched_barrier(0);
         issue_a(1);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_b(2, 2);
+        __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
         // ring slot of super-step ss is ss % DB: unrolled by DB, then the tail
         static_assert(DB == 3, "unrolled for a ring of three");
