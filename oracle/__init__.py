@@ -57,6 +57,14 @@ def _load():
     lib.orc_copy_vjp.argtypes = [i32, i32, i32, vp, vp, vp]
     lib.orc_awq_input_backward.argtypes = [i32, i32, i32, vp, i32, vp, i32, i32, vp, vp, vp,
                                            i32, vp]
+    lib.orc_dispatch_backward.argtypes = [i32, i32, i32, vp, i32, vp, vp]
+    lib.orc_dispatch_weights_backward.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+    lib.orc_combine_backward.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp, vp, vp]
+    lib.orc_swiglu_backward.argtypes = [C.c_size_t, vp, vp, vp, i32, C.c_double, C.c_double,
+                                        C.c_double, vp, vp]
+    lib.orc_awq_swiglu_input_backward.argtypes = [i32, i32, i32, vp, i32, vp, i32, i32,
+                                                  vp, vp, vp, vp, vp, vp, i32, vp, vp,
+                                                  C.c_double, C.c_double, C.c_double, vp, vp]
     lib.orc_e2m1_value.restype = C.c_double
     lib.orc_e2m1_value.argtypes = [i32]
     lib.orc_e8m0_value.restype = C.c_double
@@ -232,6 +240,84 @@ def awq_input_backward(grad, gdt, row_experts, qweight, qzeros, scales, sdt, g):
     out = np.zeros((A, K), NP_STORAGE[gdt])
     _load().orc_awq_input_backward(A, K, N, _p(grad), DT[gdt], _p(rex), E, g, _p(qweight),
                                    _p(qzeros), _p(scales), DT[sdt], _p(out))
+    return out
+
+
+# ---------------------------------------------------------------- backward path
+def dispatch_backward(dvalues, adt, slot_pos):
+    """COPY VJP: dx[t] = round_adt(fp32 sum of the token's gradient rows in
+    ascending sorted position)."""
+    dvalues = _store(dvalues, adt)
+    slot_pos = _c(slot_pos, np.int32)
+    T, k = slot_pos.shape
+    K = dvalues.shape[1]
+    dx = np.zeros((T, K), NP_STORAGE[adt])
+    _load().orc_dispatch_backward(T, k, K, _p(dvalues), DT[adt], _p(slot_pos), _p(dx))
+    return dx
+
+
+def dispatch_weights_backward(selected, weights, dweights, E):
+    """Fixed-selection logit VJP of the softmax weights: dlogits [T, E] fp32."""
+    selected = _c(selected, np.uint32)
+    weights = _c(weights, np.float32)
+    dweights = _c(dweights, np.float32)
+    T, k = selected.shape
+    dl = np.zeros((T, E), np.float32)
+    _load().orc_dispatch_weights_backward(T, E, k, _p(selected), _p(weights), _p(dweights),
+                                          _p(dl))
+    return dl
+
+
+def combine_backward(y, adt, weights, slot_pos, dout, want_dy=True, want_dweights=True):
+    """Combine VJP: (dy [A, K] adt or None, dweights [T, k] fp32 or None)."""
+    y = _store(y, adt)
+    weights = _c(weights, np.float32)
+    slot_pos = _c(slot_pos, np.int32)
+    dout = _store(dout, adt)
+    T, k = slot_pos.shape
+    K = y.shape[1]
+    dy = np.zeros_like(y) if want_dy else None
+    dw = np.zeros((T, k), np.float32) if want_dweights else None
+    _load().orc_combine_backward(T, k, K, _p(y), DT[adt], _p(weights), _p(slot_pos), _p(dout),
+                                 _p(dy), _p(dw))
+    return dy, dw
+
+
+def swiglu_backward(G, U, dh, adt, clamp=0.0, alpha=1.0, up_offset=0.0):
+    """SwiGLU VJP at the forward's storage-rounded G, U: (dG, dU) in adt."""
+    G = _store(G, adt)
+    U = _store(U, adt)
+    dh = _store(dh, adt)
+    dG = np.zeros_like(G)
+    dU = np.zeros_like(G)
+    _load().orc_swiglu_backward(G.size, _p(G), _p(U), _p(dh), DT[adt], float(clamp),
+                                float(alpha), float(up_offset), _p(dG), _p(dU))
+    return dG, dU
+
+
+def awq_swiglu_input_backward(values, adt, row_experts, gate, up, sdt, g, dh, clamp=0.0,
+                              alpha=1.0, up_offset=0.0):
+    """Input VJP of the gate/up + SwiGLU part: dvalues [A, K] adt.
+    gate / up: (qweight, qzeros, scales, bias or None) of equal shape."""
+    values = _store(values, adt)
+    A, K = values.shape
+    gqw, gqz, gs, gb = gate
+    uqw, uqz, us, ub = up
+    gqw, uqw = _c(gqw, np.int32), _c(uqw, np.int32)
+    gqz, uqz = _c(gqz, np.int32), _c(uqz, np.int32)
+    gs, us = _store(gs, sdt), _store(us, sdt)
+    gb = None if gb is None else _store(gb, sdt)
+    ub = None if ub is None else _store(ub, sdt)
+    E, K2, W8 = gqw.shape
+    assert K2 == K
+    I = W8 * 8
+    dh = _store(dh, adt)
+    rex = None if row_experts is None else _c(row_experts, np.uint32)
+    out = np.zeros((A, K), NP_STORAGE[adt])
+    _load().orc_awq_swiglu_input_backward(A, K, I, _p(values), DT[adt], _p(rex), E, g,
+                                          _p(gqw), _p(gqz), _p(gs), _p(uqw), _p(uqz), _p(us),
+                                          DT[sdt], _p(gb), _p(ub), float(clamp), float(alpha),
+                                          float(up_offset), _p(dh), _p(out))
     return out
 
 

@@ -28,6 +28,16 @@
  *   orc_combine                     order-sensitive fp32 case, k*x identity
  *   orc_copy_vjp                    adjoint identity with the COPY dispatch
  *   orc_awq_input_backward          adjoint identity, numpy matmul
+ *   orc_dispatch_backward           adjoint identity with the COPY dispatch,
+ *                                   order-sensitive fp32 case
+ *   orc_dispatch_weights_backward   finite differences of a float64 softmax,
+ *                                   two-expert closed form, zero sum
+ *   orc_combine_backward            adjoint identity and exact finite
+ *                                   differences of the combine
+ *   orc_swiglu_backward             finite differences of the closed form,
+ *                                   values at 0 and beyond the clamp
+ *   orc_awq_swiglu_input_backward   finite differences of the gate/up + SwiGLU
+ *                                   forward (fp32 activations)
  *   orc_e2m1_value, orc_e8m0_value  OCP MX element/scale tables
  *   orc_mxfp4_*                     golden byte, numpy matmul
  *   orc_moe_forward                 per-token dense float64 evaluation in numpy
@@ -489,6 +499,186 @@ void orc_awq_input_backward(int A, int K, int N, const void *grad, int gdt,
         }
     }
     free(W);
+}
+
+/* ------------------------------------------------------------------ */
+/* backward path (first order)                                          */
+/* ------------------------------------------------------------------ */
+
+/* Token t's slots in ascending sorted position, which is ascending expert ID
+ * (insertion sort; positions of one token are distinct). */
+static void slots_by_position(int k, const int32_t *pos_t, int *order)
+{
+    for (int j = 0; j < k; ++j)
+        order[j] = j;
+    for (int a = 1; a < k; ++a) {
+        int v = order[a], b = a - 1;
+        while (b >= 0 && pos_t[order[b]] > pos_t[v]) {
+            order[b + 1] = order[b];
+            --b;
+        }
+        order[b + 1] = v;
+    }
+}
+
+/* moe_exchange.rs MoeDispatchOps::moe_dispatch_backward: the COPY VJP sums the
+ * selected expert-row seeds of a token without multiplying routing weights
+ * again.  Reading (as for the combine): an fp32 sum in ascending expert ID,
+ * i.e. ascending sorted position, from 0, then one rounding to the storage
+ * type. */
+void orc_dispatch_backward(int T, int k, int K, const void *dvalues, int adt,
+                           const int32_t *slot_pos, void *dx)
+{
+#pragma omp parallel
+    {
+        int *order = (int *)malloc(sizeof(int) * (size_t)k);
+#pragma omp for schedule(static)
+        for (int t = 0; t < T; ++t) {
+            slots_by_position(k, slot_pos + (size_t)t * k, order);
+            for (int c = 0; c < K; ++c) {
+                float acc = 0.0f;
+                for (int a = 0; a < k; ++a) {
+                    size_t p = (size_t)slot_pos[(size_t)t * k + order[a]];
+                    acc = acc + (float)orc_load(dvalues, adt, p * K + c);
+                }
+                orc_store(dx, adt, (size_t)t * K + c, (double)acc);
+            }
+        }
+        free(order);
+    }
+}
+
+/* moe_exchange.rs MoeDispatchOps::moe_dispatch_weights_backward: the
+ * fixed-selection source-logit VJP of the FP32 continuous weights.  With the
+ * selection held fixed, w_j is the softmax over the selected scores, so
+ * d s_j = w_j * (dw_j - sum_i w_i dw_i), and an unselected logit gets 0 (a
+ * discrete selection has no derivative).  Readings: the stored fp32 weights
+ * stand for the softmax values; the sum runs over the slots in slot order, in
+ * double; one rounding to fp32.  The gradient of the added expert bias is the
+ * column sum of dlogits and is not formed here. */
+void orc_dispatch_weights_backward(int T, int E, int k, const uint32_t *selected,
+                                   const float *weights, const float *dweights,
+                                   float *dlogits)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        const float *w = weights + (size_t)t * k, *dw = dweights + (size_t)t * k;
+        double sum = 0.0;
+        for (int i = 0; i < k; ++i)
+            sum += (double)w[i] * (double)dw[i];
+        for (int e = 0; e < E; ++e)
+            dlogits[(size_t)t * E + e] = 0.0f;
+        for (int j = 0; j < k; ++j)
+            dlogits[(size_t)t * E + selected[(size_t)t * k + j]] =
+                (float)((double)w[j] * ((double)dw[j] - sum));
+    }
+}
+
+/* moe_exchange.rs MoeDispatchOps::moe_combine_backward with a
+ * MoeCombineSelection: only the requested derivatives are formed (NULL = not
+ * requested).  Expert rows: the combine's acc = fma(w, y, acc) has derivative
+ * w with respect to y, so dy[p,:] = round_adt(fl32(w[t,j] * dout[t,:])) for
+ * the sorted row p of assignment (t,j), one fp32 product (the final storage
+ * rounding of the forward passes the gradient through).  FP32 weights:
+ * dweights[t,j] = round_fp32(sum_c dout[t,c] * y[p,c]), summed in double. */
+void orc_combine_backward(int T, int k, int K, const void *y, int adt,
+                          const float *weights, const int32_t *slot_pos,
+                          const void *dout, void *dy, float *dweights)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            size_t p = (size_t)slot_pos[(size_t)t * k + j];
+            float w = weights[(size_t)t * k + j];
+            double acc = 0.0;
+            for (int c = 0; c < K; ++c) {
+                double g = orc_load(dout, adt, (size_t)t * K + c);
+                if (dy)
+                    orc_store(dy, adt, p * K + c, (double)(w * (float)g));
+                acc += g * orc_load(y, adt, p * K + c);
+            }
+            if (dweights)
+                dweights[(size_t)t * k + j] = (float)acc;
+        }
+    }
+}
+
+/* packed_experts.rs FrozenPackedExpertOps::packed_swiglu_input_backward, the
+ * SwiGLU step: derivatives of h = g' * sigmoid(alpha g') * (u' + up_offset)
+ * at the storage-rounded G and U of the forward, g' and u' being G and U
+ * clamped to [-c, c] when c > 0:
+ *   dG = dh * (u' + up_offset) * (s + alpha g' s (1 - s)),  s = sigmoid(alpha g')
+ *   dU = dh * g' * s
+ * Readings: the storage roundings of the forward pass the gradient through; a
+ * clamped value has derivative 1 on the closed interval [-c, c] and 0
+ * outside it; dG and dU are evaluated in double and stored in the activation
+ * type, like the forward's intermediates. */
+void orc_swiglu_backward(size_t n, const void *G, const void *U, const void *dh, int adt,
+                         double clamp, double alpha, double up_offset, void *dG, void *dU)
+{
+#pragma omp parallel for schedule(static)
+    for (size_t i = 0; i < n; ++i) {
+        double g = orc_load(G, adt, i), u = orc_load(U, adt, i), d = orc_load(dh, adt, i);
+        double gp = g, up = u, gpass = 1.0, upass = 1.0;
+        if (clamp > 0.0) {
+            gp = fmin(fmax(g, -clamp), clamp);
+            up = fmin(fmax(u, -clamp), clamp);
+            gpass = (g >= -clamp && g <= clamp) ? 1.0 : 0.0;
+            upass = (u >= -clamp && u <= clamp) ? 1.0 : 0.0;
+        }
+        double sg = 1.0 / (1.0 + exp(-alpha * gp));
+        orc_store(dG, adt, i, gpass * d * (up + up_offset) * (sg + alpha * gp * sg * (1.0 - sg)));
+        orc_store(dU, adt, i, upass * d * gp * sg);
+    }
+}
+
+/* packed_experts.rs FrozenPackedExpertOps::packed_swiglu_input_backward, the
+ * gate/up part of the chain (its down part is orc_awq_input_backward): G and U
+ * recomputed as in the forward (storage rounded), dG and dU from
+ * orc_swiglu_backward, then the transposes of both rounded packed cubes:
+ *   dvalues[p,k] = round_adt( sum_n dG[p,n] Wg_e[k,n] + sum_n dU[p,n] Wu_e[k,n] )
+ * in double, gate sum first. */
+void orc_awq_swiglu_input_backward(int A, int K, int I, const void *values, int adt,
+                                   const uint32_t *row_experts, int E, int g,
+                                   const int32_t *gqw, const int32_t *gqz, const void *gs,
+                                   const int32_t *uqw, const int32_t *uqz, const void *us,
+                                   int sdt, const void *gbias, const void *ubias,
+                                   double clamp, double alpha, double up_offset,
+                                   const void *dh, void *dvalues)
+{
+    size_t sz = (adt == ORC_F32 ? 4 : 2) * (size_t)A * I;
+    void *G = malloc(sz), *U = malloc(sz), *dG = malloc(sz), *dU = malloc(sz);
+    double *Wg = (double *)malloc(sizeof(double) * (size_t)K * I);
+    double *Wu = (double *)malloc(sizeof(double) * (size_t)K * I);
+    orc_awq_project(A, K, I, values, adt, row_experts, E, g, gqw, gqz, gs, sdt, gbias, G, NULL);
+    orc_awq_project(A, K, I, values, adt, row_experts, E, g, uqw, uqz, us, sdt, ubias, U, NULL);
+    orc_swiglu_backward((size_t)A * I, G, U, dh, adt, clamp, alpha, up_offset, dG, dU);
+    for (int e = 0; e < E; ++e) {
+        if (!expert_has_rows(A, row_experts, e))
+            continue;
+        awq_expert_dense(K, I, g, gqw, gqz, gs, sdt, e, Wg);
+        awq_expert_dense(K, I, g, uqw, uqz, us, sdt, e, Wu);
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int p = 0; p < A; ++p) {
+            int pe = row_experts ? (int)row_experts[p] : 0;
+            if (pe != e)
+                continue;
+            for (int k = 0; k < K; ++k) {
+                double ag = 0.0, au = 0.0;
+                for (int n = 0; n < I; ++n) {
+                    ag += orc_load(dG, adt, (size_t)p * I + n) * Wg[(size_t)k * I + n];
+                    au += orc_load(dU, adt, (size_t)p * I + n) * Wu[(size_t)k * I + n];
+                }
+                orc_store(dvalues, adt, (size_t)p * K + k, ag + au);
+            }
+        }
+    }
+    free(G);
+    free(U);
+    free(dG);
+    free(dU);
+    free(Wg);
+    free(Wu);
 }
 
 /* ------------------------------------------------------------------ */

@@ -96,6 +96,31 @@ void orc_awq_input_backward(int A, int K, int N, const void *grad, int gdt,
                             const int32_t *qweight, const int32_t *qzeros,
                             const void *scales, int sdt, void *grad_in);
 
+/* backward path (first order) */
+/* COPY VJP in the combine's arithmetic: dx[t,:] = round_adt(fp32 sum of the
+ * token's gradient rows in ascending sorted position) */
+void orc_dispatch_backward(int T, int k, int K, const void *dvalues, int adt,
+                           const int32_t *slot_pos, void *dx);
+/* fixed-selection logit VJP of the softmax weights: dlogits [T,E] f32 */
+void orc_dispatch_weights_backward(int T, int E, int k, const uint32_t *selected,
+                                   const float *weights, const float *dweights,
+                                   float *dlogits);
+/* combine VJP: dy [A,K] adt and dweights [T,k] f32, each nullable */
+void orc_combine_backward(int T, int k, int K, const void *y, int adt,
+                          const float *weights, const int32_t *slot_pos,
+                          const void *dout, void *dy, float *dweights);
+/* SwiGLU VJP at the forward's G, U: dG, dU [n] adt */
+void orc_swiglu_backward(size_t n, const void *G, const void *U, const void *dh, int adt,
+                         double clamp, double alpha, double up_offset, void *dG, void *dU);
+/* input VJP of the gate/up + SwiGLU part: dvalues [A,K] adt from dh [A,I] adt */
+void orc_awq_swiglu_input_backward(int A, int K, int I, const void *values, int adt,
+                                   const uint32_t *row_experts, int E, int g,
+                                   const int32_t *gqw, const int32_t *gqz, const void *gs,
+                                   const int32_t *uqw, const int32_t *uqz, const void *us,
+                                   int sdt, const void *gbias, const void *ubias,
+                                   double clamp, double alpha, double up_offset,
+                                   const void *dh, void *dvalues);
+
 /* MXFP4 bank */
 double orc_e2m1_value(int nibble);
 double orc_e8m0_value(int byte);

@@ -58,6 +58,32 @@ def test_dispatch_bit_exact_full_size(name):
     assert sum(moeq.moe_dispatch_counts(r, [0, p["E"]])) == p["T"] * p["k"]
 
 
+@pytest.mark.parametrize("T,E,k", [(700, 2048, 6), (513, 1024, 32), (257, 2048, 1)])
+def test_dispatch_many_experts_many_blocks(T, E, k):
+    """Large-batch dispatch at the expert limit: several 256-token blocks with
+    a ragged last block, per-wave token masks of 2048 experts (64 KiB of LDS),
+    top_k up to the limit; a skewing bias piles tokens onto a few experts."""
+    rng = np.random.default_rng(T * 7 + E + k)
+    logits = rng.normal(0, 1, (T, E)).astype(np.float32)
+    bias = np.zeros(E, np.float32)
+    bias[rng.choice(E, 8, replace=False)] = 3.0
+    x = rng.normal(0, 1, (T, 48)).astype(np.float32)
+    print(f"[dispatch-large] T={T} E={E} k={k}", flush=True)
+    disp = moeq.moe_dispatch(torch.from_numpy(x).to(DEV), torch.from_numpy(logits).to(DEV),
+                             torch.from_numpy(bias).to(DEV), k)
+    torch.cuda.synchronize()
+    sel, w = oracle.route(logits, bias, k)
+    off, src, pos, rex = oracle.dispatch_index(sel, E)
+    r = disp["route"]
+    np.testing.assert_array_equal(disp["selected"].cpu().numpy().view(np.uint32), sel)
+    np.testing.assert_allclose(disp["weights"].cpu().numpy(), w, rtol=2.0 ** -23, atol=0)
+    np.testing.assert_array_equal(r.expert_offsets.cpu().numpy(), off)
+    np.testing.assert_array_equal(r.row_src.cpu().numpy(), src)
+    np.testing.assert_array_equal(r.slot_pos.cpu().numpy(), pos)
+    np.testing.assert_array_equal(disp["row_experts"].cpu().numpy().view(np.uint32), rex)
+    np.testing.assert_array_equal(disp["values"].cpu().numpy(), oracle.copy_rows(x, src))
+
+
 @pytest.mark.parametrize("T,E,k", [(300, 128, 8), (77, 16, 4), (64, 512, 10), (5, 32, 32)])
 def test_router_ties_go_to_lower_id(T, E, k):
     rng = np.random.default_rng(T + E + k)
