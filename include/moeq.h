@@ -11,6 +11,12 @@
  * plus moe_dispatch_counts (range counts on the host) and awq_input_backward
  * (input VJP through the same rounded coefficients).
  *
+ * The first-order backward path runs the forward calls' VJPs in reverse:
+ *   moe_combine_backward           expert-row and FP32 weight derivatives
+ *   awq_swiglu_input_backward      input VJP through down, SwiGLU and gate/up
+ *   moe_dispatch_backward          COPY VJP back to the source tokens
+ *   moe_dispatch_weights_backward  fixed-selection router-logit VJP
+ *
  * Sources (the pages the operations are defined on):
  *   ruda-tensor 0.21.38 src/moe_exchange.rs    -- MoeDispatched, MoeDispatchOps
  *   ruda-tensor 0.21.34 src/packed_experts.rs  -- AwqExpertOptions,
@@ -219,6 +225,75 @@ moeq_status moe_combine(const moeq_route *route, const void *y, moeq_dtype act,
 moeq_status awq_input_backward(const moeq_route *route, const void *grad,
                                moeq_dtype gdt, int32_t rows, const moeq_experts *w,
                                void *grad_in, void *stream);
+
+/*
+ * moe_combine_backward -- moe_exchange.rs MoeDispatchOps::moe_combine_backward
+ * with a MoeCombineSelection: only the requested derivatives are formed.
+ *   y [A, K] act (the rows the forward combined), weights [T, top_k] fp32,
+ *   grad [T, K] act (derivative of the combine output).
+ *   grad_y [A, K] act or NULL:
+ *       grad_y[slot_pos[t, j], :] = round_act(fl32(weights[t, j] * grad[t, :]))
+ *   grad_weights [T, top_k] fp32 or NULL:
+ *       grad_weights[t, j] = round_fp32(sum over c of grad[t, c] * y[slot_pos[t, j], c]),
+ *       products and sum in fp64 (one rounding).
+ * Both NULL: nothing to do (returns OK).  T = 0: no-op.
+ */
+moeq_status moe_combine_backward(const moeq_route *route, const void *y, moeq_dtype act,
+                                 int32_t K, const float *weights, const void *grad,
+                                 void *grad_y, float *grad_weights, void *stream);
+
+/*
+ * moe_dispatch_backward -- moe_exchange.rs MoeDispatchOps::moe_dispatch_backward:
+ * the COPY VJP.  Each token sums the derivatives of its top_k expert-sorted
+ * copies, without multiplying the routing weights again:
+ *   grad_x[t, :] = round_act( fp32 sum, in ascending expert ID, of
+ *                  grad[slot_pos[t, j], :] )  from 0.
+ *   grad [A, K] act, grad_x [T, K] act.
+ */
+moeq_status moe_dispatch_backward(const moeq_route *route, const void *grad, moeq_dtype act,
+                                  int32_t K, void *grad_x, void *stream);
+
+/*
+ * moe_dispatch_weights_backward -- moe_exchange.rs MoeDispatchOps::
+ * moe_dispatch_weights_backward: the source-logit VJP of the FP32 weights with
+ * the discrete selection held fixed.  With w the softmax over the selected
+ * scores,
+ *   grad_logits[t, selected[t, j]] = round_fp32( w_j * (dw_j - sum_i w_i dw_i) )
+ * evaluated in fp64 (the sum in slot order); every unselected logit gets 0.
+ *   selected [T, top_k] u32 and weights [T, top_k] fp32 from moe_dispatch,
+ *   grad_weights [T, top_k] fp32, grad_logits [T, E] fp32 (fully written).
+ * The derivative of an added expert bias is the column sum of grad_logits.
+ */
+moeq_status moe_dispatch_weights_backward(const moeq_route *route, const uint32_t *selected,
+                                          const float *weights, const float *grad_weights,
+                                          float *grad_logits, void *stream);
+
+/*
+ * awq_swiglu_input_backward -- packed_experts.rs FrozenPackedExpertOps::
+ * packed_swiglu_input_backward: the first-order input VJP through the selected
+ * packed chain gate/up -> SwiGLU -> down, no weight / scale / bias gradients
+ * (PackedExpertAutodiffError: metadata frozen, first order only).
+ *   dh = round_act(grad . Wd_e^T)                      (as awq_input_backward)
+ *   G, U recomputed as in awq_grouped_swiglu (rounded to act), then
+ *   dG = round_act(dh * (u' + up_offset) * (s + alpha g' s (1 - s))),
+ *   dU = round_act(dh * g' * s),  s = sigmoid(alpha g'),
+ *   with g', u' the clamped G, U; a clamped value passes the derivative on
+ *   [-clamp, clamp] and blocks it outside;
+ *   grad_values = round_act(dG . Wg_e^T + dU . Wu_e^T).
+ * values [A, K] act (the forward's dispatched rows), grad [A, K] act (the
+ * derivative of the down output), grad_values [A, K] act.  gate / up / down:
+ * the forward's AWQ cubes (MXFP4 banks return EUNSUPPORTED).
+ * workspace: device, >= awq_swiglu_input_backward_workspace_bytes(A, I, act)
+ * bytes, 256-byte aligned, caller-owned; it holds dh/dG and dU between the
+ * three kernels and may be reused once the stream has passed them.
+ */
+size_t awq_swiglu_input_backward_workspace_bytes(int32_t rows, int32_t I, moeq_dtype act);
+
+moeq_status awq_swiglu_input_backward(const moeq_route *route, const void *values,
+                                      moeq_dtype act, const moeq_experts *gate,
+                                      const moeq_experts *up, const moeq_experts *down,
+                                      moeq_swiglu fn, const void *grad, void *grad_values,
+                                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static text for a status code. */
 const char *moeq_status_string(moeq_status status);

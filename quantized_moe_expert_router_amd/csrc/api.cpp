@@ -375,6 +375,8 @@ moeq_status moe_combine(const moeq_route *route, const void *y, moeq_dtype act, 
     if (st != MOEQ_OK) return st;
     if (!valid_dtype(act)) return fail(MOEQ_EDTYPE, "unknown activation dtype %d", (int)act);
     if (K < 1) return fail(MOEQ_EINVAL, "K must be positive");
+    if (route->top_k > kMaxTopK)
+        return fail(MOEQ_EUNSUPPORTED, "combine implements top_k <= %d", kMaxTopK);
     if (route->T == 0) return MOEQ_OK;
     if (!y || !weights || !out) return fail(MOEQ_EINVAL, "NULL tensor pointer");
     return device_status(launch_combine(y, act, weights, route->slot_pos, route->T, route->top_k,
@@ -418,6 +420,145 @@ moeq_status awq_input_backward(const moeq_route *route, const void *grad, moeq_d
     p.mode = PROJ_INPUT_VJP;
     return device_status(launch_proj_generic(p, static_cast<hipStream_t>(stream)),
                          "input VJP");
+}
+
+// ---------------------------------------------------------------- backward path
+
+moeq_status moe_combine_backward(const moeq_route *route, const void *y, moeq_dtype act,
+                                 int32_t K, const float *weights, const void *grad,
+                                 void *grad_y, float *grad_weights, void *stream) {
+    moeq_status st = check_route(route);
+    if (st != MOEQ_OK) return st;
+    if (!valid_dtype(act)) return fail(MOEQ_EDTYPE, "unknown activation dtype %d", (int)act);
+    if (K < 1) return fail(MOEQ_EINVAL, "K must be positive");
+    if (route->top_k > kMaxTopK)
+        return fail(MOEQ_EUNSUPPORTED, "combine VJP implements top_k <= %d", kMaxTopK);
+    if (route->T == 0 || (!grad_y && !grad_weights)) return MOEQ_OK;
+    if (!grad || !weights || !y)
+        return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    return device_status(launch_combine_backward(y, act, weights, route->slot_pos, grad, route->T,
+                                                 route->top_k, K, grad_y, grad_weights,
+                                                 static_cast<hipStream_t>(stream)),
+                         "combine backward");
+}
+
+moeq_status moe_dispatch_backward(const moeq_route *route, const void *grad, moeq_dtype act,
+                                  int32_t K, void *grad_x, void *stream) {
+    moeq_status st = check_route(route);
+    if (st != MOEQ_OK) return st;
+    if (!valid_dtype(act)) return fail(MOEQ_EDTYPE, "unknown activation dtype %d", (int)act);
+    if (K < 1) return fail(MOEQ_EINVAL, "K must be positive");
+    if (route->top_k > kMaxTopK)
+        return fail(MOEQ_EUNSUPPORTED, "COPY VJP implements top_k <= %d", kMaxTopK);
+    if (route->T == 0) return MOEQ_OK;
+    if (!grad || !grad_x) return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    return device_status(launch_dispatch_backward(grad, act, route->slot_pos, route->T,
+                                                  route->top_k, K, grad_x,
+                                                  static_cast<hipStream_t>(stream)),
+                         "dispatch backward");
+}
+
+moeq_status moe_dispatch_weights_backward(const moeq_route *route, const uint32_t *selected,
+                                          const float *weights, const float *grad_weights,
+                                          float *grad_logits, void *stream) {
+    moeq_status st = check_route(route);
+    if (st != MOEQ_OK) return st;
+    if (route->top_k > kMaxTopK)
+        return fail(MOEQ_EUNSUPPORTED, "logit VJP implements top_k <= %d", kMaxTopK);
+    if (route->T == 0) return MOEQ_OK;
+    if (!selected || !weights || !grad_weights || !grad_logits)
+        return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    return device_status(launch_weights_backward(selected, weights, grad_weights, route->T,
+                                                 route->E, route->top_k, grad_logits,
+                                                 static_cast<hipStream_t>(stream)),
+                         "weights backward");
+}
+
+size_t awq_swiglu_input_backward_workspace_bytes(int32_t rows, int32_t I, moeq_dtype act) {
+    if (rows < 0 || I < 1 || !valid_dtype(act)) return 0;
+    size_t n;
+    if (!mul_ok((size_t)rows, (size_t)I, &n) || !mul_ok(n, dtype_bytes(act), &n)) return 0;
+    return 2 * align256(n ? n : 1);
+}
+
+moeq_status awq_swiglu_input_backward(const moeq_route *route, const void *values,
+                                      moeq_dtype act, const moeq_experts *gate,
+                                      const moeq_experts *up, const moeq_experts *down,
+                                      moeq_swiglu fn, const void *grad, void *grad_values,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+    moeq_status st = check_route(route);
+    if (st != MOEQ_OK) return st;
+    if (!valid_dtype(act)) return fail(MOEQ_EDTYPE, "unknown activation dtype %d", (int)act);
+    if ((st = check_experts(gate, "gate", route->E, -1, -1, false)) != MOEQ_OK) return st;
+    const int K = gate->in_features, I = gate->out_features;
+    if ((st = check_experts(up, "up", route->E, K, I, false)) != MOEQ_OK) return st;
+    if ((st = check_experts(down, "down", route->E, I, K, false)) != MOEQ_OK) return st;
+    if (gate->format != MOEQ_FMT_AWQ || up->format != MOEQ_FMT_AWQ ||
+        down->format != MOEQ_FMT_AWQ)
+        return fail(MOEQ_EUNSUPPORTED, "the chain VJP is implemented for AWQ cubes");
+    if (up->scale_dtype != gate->scale_dtype || up->group_size != gate->group_size)
+        return fail(MOEQ_EDTYPE, "gate and up must share scale dtype and group size");
+    if ((up->bias == nullptr) != (gate->bias == nullptr))
+        return fail(MOEQ_EINVAL, "gate and up must both have or both lack a bias");
+    if (act == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 activations are not implemented");
+    if (!(fn.clamp >= 0.0f) || !(fn.alpha == fn.alpha) || !(fn.up_offset == fn.up_offset))
+        return fail(MOEQ_EINVAL, "bad SwiGLU parameters");
+    const int A = route->T * route->top_k;
+    const size_t need = awq_swiglu_input_backward_workspace_bytes(A, I, act);
+    if (need == 0) return fail(MOEQ_ESHAPE, "size overflow");
+    if (A == 0) return MOEQ_OK;
+    if (!values || !grad || !grad_values) return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    if (!workspace) return fail(MOEQ_EINVAL, "workspace is NULL");
+    if ((uintptr_t)workspace % 256 != 0)
+        return fail(MOEQ_EWORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(MOEQ_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    char *dg = static_cast<char *>(workspace);  // dh, then dG in place
+    char *du = dg + need / 2;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ProjProblem p{};
+    p.offsets = route->expert_offsets;
+    p.tile_offsets = route->tile_offsets;
+    p.tile_expert = route->tile_expert;
+    p.rows = A;
+    p.E = route->E;
+    p.act = act;
+    p.clamp = fn.clamp;
+    p.alpha = fn.alpha;
+    p.up_offset = fn.up_offset;
+    // dh = grad . Wd^T
+    ProjProblem q = p;
+    q.in = grad;
+    q.out = dg;
+    q.Kred = K;
+    q.Nout = I;
+    q.w0 = operand_of(down);
+    q.w1 = q.w0;
+    q.mode = PROJ_INPUT_VJP;
+    if ((st = device_status(launch_proj_generic(q, s), "down input VJP")) != MOEQ_OK) return st;
+    // G, U recomputed; dG over dh, dU
+    q = p;
+    q.in = values;
+    q.in2 = dg;
+    q.out = dg;
+    q.out2 = du;
+    q.Kred = K;
+    q.Nout = I;
+    q.w0 = operand_of(gate);
+    q.w1 = operand_of(up);
+    q.mode = PROJ_SWIGLU_VJP;
+    if ((st = device_status(launch_proj_generic(q, s), "SwiGLU VJP")) != MOEQ_OK) return st;
+    // grad_values = dG . Wg^T + dU . Wu^T
+    q = p;
+    q.in = dg;
+    q.in2 = du;
+    q.out = grad_values;
+    q.Kred = I;
+    q.Nout = K;
+    q.w0 = operand_of(gate);
+    q.w1 = operand_of(up);
+    q.mode = PROJ_INPUT_VJP2;
+    return device_status(launch_proj_generic(q, s), "gate/up input VJP");
 }
 
 }  // extern "C"

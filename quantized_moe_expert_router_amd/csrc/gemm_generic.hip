@@ -57,9 +57,28 @@ __device__ __forceinline__ float swiglu(float g, float u, float clamp, float alp
     return g * (1.0f / (1.0f + expf(-alpha * g))) * (u + off);
 }
 
+// Derivatives of h = g' sigmoid(alpha g') (u' + off) at the rounded G, U (g', u'
+// clamped when clamp > 0; a clamped value passes the derivative on the closed
+// interval and blocks it outside).
+__device__ __forceinline__ void swiglu_vjp(float g, float u, float d, float clamp, float alpha,
+                                           float off, float *dg, float *du) {
+    float gpass = 1.0f, upass = 1.0f;
+    if (clamp > 0.0f) {
+        gpass = (g >= -clamp && g <= clamp) ? 1.0f : 0.0f;
+        upass = (u >= -clamp && u <= clamp) ? 1.0f : 0.0f;
+        g = fminf(fmaxf(g, -clamp), clamp);
+        u = fminf(fmaxf(u, -clamp), clamp);
+    }
+    const float sg = 1.0f / (1.0f + expf(-alpha * g));
+    *dg = gpass * d * (u + off) * (sg + alpha * g * sg * (1.0f - sg));
+    *du = upass * d * g * sg;
+}
+
 template <int ACT, int SD, int MODE>
 __global__ __launch_bounds__(256) void proj_generic_kernel(ProjProblem p) {
+    constexpr bool two_in = MODE == PROJ_INPUT_VJP2;
     __shared__ float xs[kRowChunk][kKTile + 1];
+    __shared__ float xs2[two_in ? kRowChunk : 1][kKTile + 1];
     const int e = blockIdx.y;
     int r0 = 0, r1 = p.rows;
     if (p.offsets) {
@@ -70,7 +89,8 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(ProjProblem p) {
     const int tid = threadIdx.x, cl = tid & (kCols - 1), rg = tid >> 6;
     const int col = blockIdx.x * kCols + cl;
     const bool col_ok = col < p.Nout;
-    const bool two = (MODE == PROJ_SWIGLU || MODE == PROJ_BANK_SWIGLU);
+    const bool two = (MODE == PROJ_SWIGLU || MODE == PROJ_BANK_SWIGLU ||
+                      MODE == PROJ_SWIGLU_VJP || MODE == PROJ_INPUT_VJP2);
 
     for (int rc = r0; rc < r1; rc += kRowChunk) {
         float acc0[4] = {0.f, 0.f, 0.f, 0.f}, acc1[4] = {0.f, 0.f, 0.f, 0.f};
@@ -81,6 +101,10 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(ProjProblem p) {
                 const int row = rc + rr, kx = k0 + kk;
                 xs[rr][kk] = (row < r1 && kx < p.Kred) ? load_f<ACT>(p.in, (size_t)row * p.Kred + kx)
                                                       : 0.0f;
+                if (two_in)
+                    xs2[rr][kk] = (row < r1 && kx < p.Kred)
+                                      ? load_f<ACT>(p.in2, (size_t)row * p.Kred + kx)
+                                      : 0.0f;
             }
             __syncthreads();
             if (!col_ok) continue;
@@ -91,12 +115,15 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(ProjProblem p) {
                 if (MODE == PROJ_PLAIN) {
                     c0 = p.w0.format == MOEQ_FMT_AWQ ? awq_coeff<SD>(p.w0, e, kx, col)
                                                      : mxfp4_coeff(p.w0, e, col, kx);
-                } else if (MODE == PROJ_SWIGLU) {
+                } else if (MODE == PROJ_SWIGLU || MODE == PROJ_SWIGLU_VJP) {
                     c0 = awq_coeff<SD>(p.w0, e, kx, col);
                     c1 = awq_coeff<SD>(p.w1, e, kx, col);
                 } else if (MODE == PROJ_BANK_SWIGLU) {
                     c0 = mxfp4_coeff(p.w0, e, 2 * col, kx);
                     c1 = mxfp4_coeff(p.w0, e, 2 * col + 1, kx);
+                } else if (MODE == PROJ_INPUT_VJP2) {  // output column = input feature
+                    c0 = awq_coeff<SD>(p.w0, e, col, kx);
+                    c1 = awq_coeff<SD>(p.w1, e, col, kx);
                 } else {  // PROJ_INPUT_VJP: output column = input feature of W
                     c0 = awq_coeff<SD>(p.w0, e, col, kx);
                 }
@@ -104,7 +131,10 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(ProjProblem p) {
                 for (int i = 0; i < 4; ++i) {
                     const float xv = xs[rg + 4 * i][kk];
                     acc0[i] = __builtin_fmaf(xv, c0, acc0[i]);
-                    if (two) acc1[i] = __builtin_fmaf(xv, c1, acc1[i]);
+                    if (two_in)
+                        acc1[i] = __builtin_fmaf(xs2[rg + 4 * i][kk], c1, acc1[i]);
+                    else if (two)
+                        acc1[i] = __builtin_fmaf(xv, c1, acc1[i]);
                 }
             }
         }
@@ -124,6 +154,16 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(ProjProblem p) {
                 const float g = round_to<ACT>(acc0[i] + bias_value<SD>(p.w0, e, 2 * col));
                 const float u = round_to<ACT>(acc1[i] + bias_value<SD>(p.w0, e, 2 * col + 1));
                 v = swiglu(g, u, p.clamp, p.alpha, p.up_offset);
+            } else if (MODE == PROJ_SWIGLU_VJP) {
+                const size_t at = (size_t)row * p.Nout + col;
+                const float g = round_to<ACT>(acc0[i] + bias_value<SD>(p.w0, e, col));
+                const float u = round_to<ACT>(acc1[i] + bias_value<SD>(p.w1, e, col));
+                const float d = load_f<ACT>(p.in2, at);  // read before out (may alias) is written
+                float du;
+                swiglu_vjp(g, u, d, p.clamp, p.alpha, p.up_offset, &v, &du);
+                store_f<ACT>(p.out2, at, du);
+            } else if (MODE == PROJ_INPUT_VJP2) {
+                v = acc0[i] + acc1[i];  // gate part, then up part
             } else {
                 v = acc0[i];
             }
@@ -144,6 +184,14 @@ hipError_t launch_mode(const ProjProblem &p, hipStream_t s) {
         break;
     case PROJ_BANK_SWIGLU:
         hipLaunchKernelGGL((proj_generic_kernel<ACT, SD, PROJ_BANK_SWIGLU>), grid, block, 0, s,
+                           p);
+        break;
+    case PROJ_SWIGLU_VJP:
+        hipLaunchKernelGGL((proj_generic_kernel<ACT, SD, PROJ_SWIGLU_VJP>), grid, block, 0, s,
+                           p);
+        break;
+    case PROJ_INPUT_VJP2:
+        hipLaunchKernelGGL((proj_generic_kernel<ACT, SD, PROJ_INPUT_VJP2>), grid, block, 0, s,
                            p);
         break;
     default:

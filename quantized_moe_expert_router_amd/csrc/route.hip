@@ -502,8 +502,10 @@ hipError_t launch_copy_rows(const void *x, size_t row_bytes, int A, const int32_
 // ID; every column then runs acc = fma(w, y, acc) in that order.  Each thread
 // owns VEC consecutive columns and moves them as one 16-byte vector; its row
 // loads are all issued before the first fma (KM >= k bounds them at compile
-// time).
-template <int ACT, int KM>
+// time).  WEIGHTED = false is the COPY VJP (moe_exchange.rs
+// MoeDispatchOps::moe_dispatch_backward): w = 1, so fma(1, y, acc) is the plain
+// fp32 sum acc + y in the same ascending order, and `weights` is not read.
+template <int ACT, int KM, bool WEIGHTED>
 __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y,
                                                       const float *__restrict__ weights,
                                                       const int32_t *__restrict__ slot_pos,
@@ -519,7 +521,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ y
     const int t = blockIdx.x;
     if ((int)threadIdx.x < k) {
         raw_s[threadIdx.x] = slot_pos[(size_t)t * k + threadIdx.x];
-        wraw_s[threadIdx.x] = weights[(size_t)t * k + threadIdx.x];
+        wraw_s[threadIdx.x] = WEIGHTED ? weights[(size_t)t * k + threadIdx.x] : 1.0f;
     }
     __syncthreads();
     if ((int)threadIdx.x < k) {
@@ -572,8 +574,8 @@ hipError_t launch_combine(const void *y, int act, const float *weights,
     const bool vec_ok = ((uintptr_t)y | (uintptr_t)out) % 16 == 0 && K % vec == 0;
     int threads = vec_ok ? K / vec : K;
     threads = threads >= 256 ? 256 : ((threads + 63) / 64) * 64;
-#define MOEQ_COMBINE(DT, KM)                                                               \
-    hipLaunchKernelGGL((combine_kernel<DT, KM>), dim3(T), dim3(threads), 0, s, y, weights,   \
+#define MOEQ_COMBINE(DT, KM)                                                                 \
+    hipLaunchKernelGGL((combine_kernel<DT, KM, true>), dim3(T), dim3(threads), 0, s, y, weights, \
                        slot_pos, T, k, K, vec_ok, out)
 #define MOEQ_COMBINE_K(DT)            \
     if (k <= 8)                       \
@@ -590,6 +592,34 @@ hipError_t launch_combine(const void *y, int act, const float *weights,
         MOEQ_COMBINE_K(MOEQ_F16);
 #undef MOEQ_COMBINE_K
 #undef MOEQ_COMBINE
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_backward(const void *grad, int act, const int32_t *slot_pos, int T,
+                                    int k, int K, void *grad_x, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const int vec = act == MOEQ_F32 ? 4 : 8;
+    const bool vec_ok = ((uintptr_t)grad | (uintptr_t)grad_x) % 16 == 0 && K % vec == 0;
+    int threads = vec_ok ? K / vec : K;
+    threads = threads >= 256 ? 256 : ((threads + 63) / 64) * 64;
+#define MOEQ_COPY_VJP(DT, KM)                                                                 \
+    hipLaunchKernelGGL((combine_kernel<DT, KM, false>), dim3(T), dim3(threads), 0, s, grad,     \
+                       nullptr, slot_pos, T, k, K, vec_ok, grad_x)
+#define MOEQ_COPY_VJP_K(DT)           \
+    if (k <= 8)                       \
+        MOEQ_COPY_VJP(DT, 8);         \
+    else if (k <= 16)                 \
+        MOEQ_COPY_VJP(DT, 16);        \
+    else                              \
+        MOEQ_COPY_VJP(DT, kMaxTopK)
+    if (act == MOEQ_F32)
+        MOEQ_COPY_VJP_K(MOEQ_F32);
+    else if (act == MOEQ_BF16)
+        MOEQ_COPY_VJP_K(MOEQ_BF16);
+    else
+        MOEQ_COPY_VJP_K(MOEQ_F16);
+#undef MOEQ_COPY_VJP_K
+#undef MOEQ_COPY_VJP
     return hipGetLastError();
 }
 

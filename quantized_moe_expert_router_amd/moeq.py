@@ -27,7 +27,9 @@ _DT_TORCH = {v: k for k, v in _TORCH_DT.items()}
 # every symbol include/moeq.h declares
 EXPORTS = ("moeq_route_workspace_bytes", "moeq_route_bind", "moe_dispatch",
            "moe_dispatch_counts", "awq_grouped_swiglu", "awq_grouped_down", "moe_combine",
-           "awq_input_backward", "moeq_status_string", "moeq_last_error")
+           "awq_input_backward", "moe_combine_backward", "moe_dispatch_backward",
+           "moe_dispatch_weights_backward", "awq_swiglu_input_backward_workspace_bytes",
+           "awq_swiglu_input_backward", "moeq_status_string", "moeq_last_error")
 
 
 class MoeqError(RuntimeError):
@@ -91,6 +93,18 @@ def lib():
     L.awq_input_backward.restype = C.c_int
     L.awq_input_backward.argtypes = [C.POINTER(Route), vp, C.c_int, i32, C.POINTER(Experts),
                                      vp, vp]
+    L.moe_combine_backward.restype = C.c_int
+    L.moe_combine_backward.argtypes = [C.POINTER(Route), vp, C.c_int, i32, vp, vp, vp, vp, vp]
+    L.moe_dispatch_backward.restype = C.c_int
+    L.moe_dispatch_backward.argtypes = [C.POINTER(Route), vp, C.c_int, i32, vp, vp]
+    L.moe_dispatch_weights_backward.restype = C.c_int
+    L.moe_dispatch_weights_backward.argtypes = [C.POINTER(Route), vp, vp, vp, vp, vp]
+    L.awq_swiglu_input_backward_workspace_bytes.restype = C.c_size_t
+    L.awq_swiglu_input_backward_workspace_bytes.argtypes = [i32, i32, C.c_int]
+    L.awq_swiglu_input_backward.restype = C.c_int
+    L.awq_swiglu_input_backward.argtypes = [C.POINTER(Route), vp, C.c_int, C.POINTER(Experts),
+                                            C.POINTER(Experts), C.POINTER(Experts), SwiGLU, vp,
+                                            vp, vp, C.c_size_t, vp]
     L.moeq_status_string.restype = C.c_char_p
     L.moeq_status_string.argtypes = [C.c_int]
     L.moeq_last_error.restype = C.c_char_p
@@ -271,6 +285,73 @@ def awq_input_backward(route: Optional[RouteState], grad: torch.Tensor, w: AwqEx
                                     _dt(grad), rows, C.byref(wc), _ptr(grad_in),
                                     _stream(grad.device)))
     return grad_in
+
+
+# ------------------------------------------------------------------ backward path
+def moe_combine_backward(route: RouteState, y: torch.Tensor, weights: torch.Tensor,
+                         grad: torch.Tensor, experts: bool = True, want_weights: bool = True):
+    """Combine VJP with a MoeCombineSelection: (grad_y [A,K] or None,
+    grad_weights [T,top_k] fp32 or None); only the requested ones are formed."""
+    K = y.shape[1]
+    gy = torch.empty_like(y) if experts else None
+    gw = (torch.empty(route.T, route.top_k, dtype=torch.float32, device=y.device)
+          if want_weights else None)
+    _check(lib().moe_combine_backward(C.byref(route.c), _ptr(y), _dt(y), K, _ptr(weights),
+                                      _ptr(grad), _ptr(gy), _ptr(gw), _stream(y.device)))
+    return gy, gw
+
+
+def moe_dispatch_backward(route: RouteState, grad: torch.Tensor,
+                          grad_x: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """COPY VJP: sums each token's expert-sorted row derivatives (no weights)."""
+    K = grad.shape[1]
+    if grad_x is None:
+        grad_x = torch.empty(route.T, K, dtype=grad.dtype, device=grad.device)
+    _check(lib().moe_dispatch_backward(C.byref(route.c), _ptr(grad), _dt(grad), K, _ptr(grad_x),
+                                       _stream(grad.device)))
+    return grad_x
+
+
+def moe_dispatch_weights_backward(route: RouteState, selected: torch.Tensor,
+                                  weights: torch.Tensor, grad_weights: torch.Tensor,
+                                  grad_logits: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fixed-selection logit VJP of the FP32 routing weights: [T, E] fp32."""
+    for t in (weights, grad_weights):
+        if t.dtype != torch.float32:
+            raise MoeqError(EDTYPE, "weights and their gradient are fp32")
+    if grad_logits is None:
+        grad_logits = torch.empty(route.T, route.E, dtype=torch.float32,
+                                  device=weights.device)
+    _check(lib().moe_dispatch_weights_backward(C.byref(route.c), _ptr(selected), _ptr(weights),
+                                               _ptr(grad_weights), _ptr(grad_logits),
+                                               _stream(weights.device)))
+    return grad_logits
+
+
+def awq_swiglu_input_backward_workspace_bytes(rows: int, I: int, dtype: torch.dtype) -> int:
+    return int(lib().awq_swiglu_input_backward_workspace_bytes(rows, I,
+                                                               _TORCH_DT.get(dtype, 99)))
+
+
+def awq_swiglu_input_backward(route: RouteState, values: torch.Tensor, gate: AwqExperts,
+                              up: AwqExperts, down: AwqExperts, grad: torch.Tensor,
+                              clamp: float = 0.0, alpha: float = 1.0, up_offset: float = 0.0,
+                              workspace: Optional[torch.Tensor] = None,
+                              grad_values: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Input VJP through down, SwiGLU and gate/up (first order): [A, K] act."""
+    gc, uc, dc = gate.c(), up.c(), down.c()
+    A = values.shape[0]
+    nbytes = awq_swiglu_input_backward_workspace_bytes(A, gc.out_features, values.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=values.device)
+    if grad_values is None:
+        grad_values = torch.empty_like(values)
+    _check(lib().awq_swiglu_input_backward(C.byref(route.c), _ptr(values), _dt(values),
+                                           C.byref(gc), C.byref(uc), C.byref(dc),
+                                           SwiGLU(clamp, alpha, up_offset), _ptr(grad),
+                                           _ptr(grad_values), _ptr(workspace),
+                                           workspace.numel(), _stream(values.device)))
+    return grad_values
 
 
 def moe_ffn(x, logits, expert_bias, top_k, gate, up, down, clamp=0.0, alpha=1.0, up_offset=0.0):

@@ -199,3 +199,60 @@ def test_size_overflow_is_rejected(L):
     _, r = bind(L, 0, 1 << 30, 2)
     big = awq(E=1 << 30, K=1 << 30, N=1 << 30, g=1 << 30)
     assert swiglu(L, r, big, big) == moeq.ESHAPE
+
+
+def test_backward_path_validation(L):
+    """moe_exchange.rs MoeDispatchOps backward calls and packed_experts.rs
+    packed_swiglu_input_backward: every case below fails validation or is a no-op."""
+    P = C.c_void_p(FAKE)
+    _, r = bind(L, 4, 8, 2)
+    _, r0 = bind(L, 0, 8, 2)
+    _, r33 = bind(L, 4, 64, 33)
+    cb = lambda route, K=16, act=moeq.BF16, grad=P, gy=P, gw=P: L.moe_combine_backward(
+        C.byref(route), P, act, K, P, grad, gy, gw, None)
+    assert cb(r, K=0) == moeq.EINVAL
+    assert cb(r, act=3) == moeq.EDTYPE
+    assert cb(r, grad=None) == moeq.EINVAL
+    assert cb(r, gy=None, gw=None) == moeq.OK          # nothing requested: nothing formed
+    assert cb(r0) == moeq.OK
+    assert cb(r33) == moeq.EUNSUPPORTED
+    assert L.moe_combine_backward(C.byref(moeq.Route()), P, moeq.BF16, 16, P, P, P, P,
+                                  None) == moeq.EINVAL
+    db = lambda route, K=16, act=moeq.BF16, ptr=P: L.moe_dispatch_backward(
+        C.byref(route), ptr, act, K, ptr, None)
+    assert db(r, K=0) == moeq.EINVAL
+    assert db(r, act=9) == moeq.EDTYPE
+    assert db(r, ptr=None) == moeq.EINVAL
+    assert db(r0) == moeq.OK
+    assert db(r33) == moeq.EUNSUPPORTED
+    wb = lambda route, ptr=P: L.moe_dispatch_weights_backward(C.byref(route), ptr, ptr, ptr, ptr,
+                                                              None)
+    assert wb(r, ptr=None) == moeq.EINVAL
+    assert wb(r0) == moeq.OK
+    assert wb(r33) == moeq.EUNSUPPORTED
+    ws = L.awq_swiglu_input_backward_workspace_bytes
+    assert ws(8, 32, moeq.BF16) >= 2 * 8 * 32 * 2 and ws(8, 32, moeq.BF16) % 256 == 0
+    assert ws(0, 32, moeq.F32) > 0
+    assert ws(-1, 32, moeq.BF16) == 0 and ws(8, 0, moeq.BF16) == 0 and ws(8, 32, 7) == 0
+    need = ws(8, 32, moeq.BF16)
+
+    def sib(route, gate=None, up=None, down=None, act=moeq.BF16, fn=(0.0, 1.0, 0.0),
+            wsp=FAKE, nbytes=need):
+        gate = gate or awq(K=64, N=32)
+        up = up or awq(K=64, N=32)
+        down = down or awq(K=32, N=64)
+        return L.awq_swiglu_input_backward(C.byref(route), P, act, C.byref(gate), C.byref(up),
+                                           C.byref(down), moeq.SwiGLU(*fn), P, P,
+                                           C.c_void_p(wsp) if wsp else None, nbytes, None)
+    assert sib(r0) == moeq.OK                           # no rows: nothing enqueued
+    assert sib(r, wsp=0) == moeq.EINVAL
+    assert sib(r, wsp=FAKE + 16) == moeq.EWORKSPACE
+    assert sib(r, nbytes=need - 1) == moeq.EWORKSPACE
+    assert sib(r, down=awq(K=32, N=48)) == moeq.ESHAPE  # down must map I back to K
+    assert sib(r, up=awq(K=64, N=40)) == moeq.ESHAPE
+    assert sib(r, up=awq(K=64, N=32, sdt=moeq.F16)) == moeq.EDTYPE
+    assert sib(r, gate=awq(K=64, N=32, bias=FAKE)) == moeq.EINVAL
+    assert sib(r, down=bank(K=32, R=64, inter=0)) == moeq.EUNSUPPORTED
+    assert sib(r, act=moeq.F16) == moeq.EUNSUPPORTED
+    assert sib(r, fn=(-2.0, 1.0, 0.0)) == moeq.EINVAL
+    assert sib(r, down=awq(E=4, K=32, N=64)) == moeq.ERANGE
