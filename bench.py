@@ -11,6 +11,12 @@ cycle over the replicas in one graph -- and replayed.
 
 Prints ONE JSON line.  Default workload: the decode-shaped AWQ MoE
 (T=64, hidden 2048, intermediate 768, 128 experts, top_k 8, group 128, bf16).
+
+--path backward times the first-order backward path instead: one step =
+moe_combine_backward (expert rows + FP32 weights) -> awq_swiglu_input_backward
+(down VJP, recomputed gate/up with the SwiGLU VJP, both transposed cubes) ->
+moe_dispatch_backward -> moe_dispatch_weights_backward, on the same workload,
+with the forward's values, y and routing resident before the timed region.
 """
 from __future__ import annotations
 
@@ -27,6 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 METRIC = "MoE expert-FFN tokens/s at 1 GPU; % of HBM (decode) / MFMA (prefill) peak"
+METRIC_BWD = "MoE expert-FFN backward tokens/s at 1 GPU (first-order input VJPs)"
 
 
 def parse():
@@ -38,6 +45,7 @@ def parse():
                     choices=["tiny", "decode", "prefill", "many", "mxfp4"])
     ap.add_argument("--replica-bytes", type=float, default=1.2e9,
                     help="weight bytes cycled through by consecutive steps")
+    ap.add_argument("--path", default="forward", choices=["forward", "backward"])
     ap.add_argument("--eager", action="store_true", help="no HIP graph capture")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -84,7 +92,8 @@ def alg_bytes(p, offsets):
     act_dn = A * I * ab + A * H * ab                 # h read, y written
     act_other = T * E * 4 + T * H * ab + A * H * ab + T * k * 4 + A * H * ab + T * H * ab
     return dict(touched=touched, gateup=w_gu + act_gu, down=w_dn + act_dn,
-                total=w_gu + w_dn + act_gu + act_dn + act_other, weights=w_gu + w_dn)
+                total=w_gu + w_dn + act_gu + act_dn + act_other, weights=w_gu + w_dn,
+                w_gateup=w_gu, w_down=w_dn)
 
 
 def flops(p):
@@ -163,6 +172,49 @@ def cpu_baseline(cfg, target_s):
                       f"({el:.1f} s, double accumulation, OpenMP)"}
 
 
+def cpu_baseline_backward(cfg, target_s):
+    """The oracle's backward steps as they stand, on a bounded sample."""
+    import numpy as np
+    import oracle
+    from quantized_moe_expert_router_amd.synth import make_inputs, to_storage
+    T = cfg.T if cfg.name == "tiny" else min(cfg.T, 16)
+    p = make_inputs(cfg, T=T)
+    oracle._load()
+    ref = oracle.moe_forward(p)
+    adt, sdt, g = p["adt"], p["sdt"], p["group"]
+    gout = to_storage(np.random.default_rng(5).normal(0, 1, (T, p["H"])), adt)
+    gate = (p["gate_qw"], p["gate_qz"], p["gate_s"], p["gate_b"])
+    up = (p["up_qw"], p["up_qz"], p["up_s"], p["up_b"])
+    rex, pos = ref["row_experts"], ref["slot_pos"]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        dy, dw = oracle.combine_backward(ref["y"], adt, ref["weights"], pos, gout)
+        dh = oracle.awq_input_backward(dy, adt, rex, p["down_qw"], p["down_qz"], p["down_s"],
+                                       sdt, g)
+        dv = oracle.awq_swiglu_input_backward(ref["values"], adt, rex, gate, up, sdt, g, dh)
+        oracle.dispatch_backward(dv, adt, pos)
+        oracle.dispatch_weights_backward(ref["selected"], ref["weights"], dw, p["E"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 1000:
+            break
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    return {"value": round(reps * T / el, 3), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{reps} x full backward of a {T}-token batch of this workload "
+                      f"({el:.1f} s, double accumulation, OpenMP)"}
+
+
+def bwd_alg_bytes(p, ab_fwd):
+    """Algorithmic bytes of the chain call: the touched down cube once and the
+    touched gate/up cubes twice (the recompute of G, U reduces over the hidden
+    features, the transposed product over the intermediate ones: two passes),
+    plus values, grad and grad_values, and dh, dG, dU each written and read once."""
+    A, H, I = p["T"] * p["k"], p["H"], p["I"]
+    ab = 4 if p["adt"] == "f32" else 2
+    return ab_fwd["w_down"] + 2 * ab_fwd["w_gateup"] + 3 * A * H * ab + 6 * A * I * ab
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -223,6 +275,35 @@ def main():
         moeq.awq_grouped_down(route, h, w["down"], y)
         moeq.moe_combine(route, y, bufs["weights"], out)
 
+    backward = args.path == "backward"
+    if backward:
+        if cfg.fmt != "awq":
+            print("the backward chain is implemented for AWQ cubes", file=sys.stderr)
+            sys.exit(2)
+        step(0)   # the forward's values, y and routing, resident before timing
+        gen = torch.Generator(device=dev).manual_seed(5)
+        gout = torch.randn(T, H, generator=gen, device=dev).to(adt)
+        gy = torch.empty(A, H, dtype=adt, device=dev)
+        gw = torch.empty(T, k, dtype=torch.float32, device=dev)
+        gv = torch.empty(A, H, dtype=adt, device=dev)
+        gx = torch.empty(T, H, dtype=adt, device=dev)
+        gl = torch.empty(T, E, dtype=torch.float32, device=dev)
+        wsp = torch.empty(moeq.awq_swiglu_input_backward_workspace_bytes(A, I, adt),
+                          dtype=torch.uint8, device=dev)
+
+        def chain(w):
+            moeq.awq_swiglu_input_backward(route, bufs["values"], w["gate"], w["up_arg"],
+                                           w["down"], gy, cfg.clamp, 1.0, 0.0, wsp, gv)
+
+        def step(i):  # noqa: F811 -- the backward step replaces the forward one
+            w = replicas[i % R]
+            moeq.moe_combine_backward(route, y, bufs["weights"], gout, grad_y=gy,
+                                      grad_weights=gw)
+            chain(w)
+            moeq.moe_dispatch_backward(route, gv, gx)
+            moeq.moe_dispatch_weights_backward(route, bufs["selected"], bufs["weights"], gw,
+                                               gl)
+
     # warm-up (also before capture, on a side stream as graph capture expects)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -275,11 +356,46 @@ def main():
     for i, (a, b) in enumerate(evs):
         w = replicas[i % R]
         a.record(stream)
-        moeq.awq_grouped_swiglu(route, bufs["values"], w["gate"], w["up_arg"], cfg.clamp, 1.0,
-                                0.0, h)
+        if backward:
+            chain(w)
+        else:
+            moeq.awq_grouped_swiglu(route, bufs["values"], w["gate"], w["up_arg"], cfg.clamp,
+                                    1.0, 0.0, h)
         b.record(stream)
     torch.cuda.synchronize()
     k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    if backward:
+        offsets = route.expert_offsets.cpu().numpy()
+        ab = alg_bytes(p, offsets)
+        cb = bwd_alg_bytes(p, ab)
+        cf = 10 * A * H * I   # down VJP, gate/up recompute, two transposed products
+        ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if cf / cb > ridge:
+            bound, peak, unit = "mfma", BF16_PEAK_TFLOPS, "TFLOP/s"
+            achieved = cf / (k_ms * 1e-3) / 1e12
+        else:
+            bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+            achieved = cb / (k_ms * 1e-3) / 1e9
+        res = {
+            "metric": METRIC_BWD, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16" if cfg.adt == "bf16" else "f32",
+            "data": "synthetic",
+            "config": {"workload": workload_name(cfg), "tokens": T, "assignments": A,
+                       "touched_experts": ab["touched"], "weight_replicas": R,
+                       "graph": graphs is not None, "path": "backward"},
+            "roofline": {"kernel": "awq_swiglu_input_backward (down VJP + gate/up recompute "
+                                   "with SwiGLU VJP + transposed gate/up)",
+                         "bound": bound, "achieved": round(achieved, 1), "peak": peak,
+                         "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                         "kernel_ms": round(k_ms, 5), "alg_bytes_per_launch": cb,
+                         "alg_flops_per_launch": cf},
+        }
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_backward(cfg, args.cpu_seconds)
+        print(json.dumps(res), flush=True)
+        return
 
     offsets = route.expert_offsets.cpu().numpy()
     ab = alg_bytes(p, offsets)

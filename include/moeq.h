@@ -284,8 +284,9 @@ moeq_status moe_dispatch_weights_backward(const moeq_route *route, const uint32_
  * derivative of the down output), grad_values [A, K] act.  gate / up / down:
  * the forward's AWQ cubes (MXFP4 banks return EUNSUPPORTED).
  * workspace: device, >= awq_swiglu_input_backward_workspace_bytes(A, I, act)
- * bytes, 256-byte aligned, caller-owned; it holds dh/dG and dU between the
- * three kernels and may be reused once the stream has passed them.
+ * bytes, 256-byte aligned, caller-owned; it holds dh, G / dG and U / dU
+ * ([A, I] act each) between the call's kernels and may be reused once the
+ * stream has passed them.
  */
 size_t awq_swiglu_input_backward_workspace_bytes(int32_t rows, int32_t I, moeq_dtype act);
 

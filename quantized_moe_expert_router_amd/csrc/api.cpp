@@ -410,6 +410,8 @@ moeq_status awq_input_backward(const moeq_route *route, const void *grad, moeq_d
     p.in = grad;
     p.out = grad_in;
     p.offsets = route ? route->expert_offsets : nullptr;
+    p.tile_offsets = route ? route->tile_offsets : nullptr;
+    p.tile_expert = route ? route->tile_expert : nullptr;
     p.rows = rows;
     p.E = route ? route->E : 1;
     p.act = gdt;
@@ -418,7 +420,8 @@ moeq_status awq_input_backward(const moeq_route *route, const void *grad, moeq_d
     p.w0 = operand_of(w);
     p.w1 = p.w0;
     p.mode = PROJ_INPUT_VJP;
-    return device_status(launch_proj_generic(p, static_cast<hipStream_t>(stream)),
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return device_status(vjp_fits(p) ? launch_vjp(p, s) : launch_proj_generic(p, s),
                          "input VJP");
 }
 
@@ -478,7 +481,7 @@ size_t awq_swiglu_input_backward_workspace_bytes(int32_t rows, int32_t I, moeq_d
     if (rows < 0 || I < 1 || !valid_dtype(act)) return 0;
     size_t n;
     if (!mul_ok((size_t)rows, (size_t)I, &n) || !mul_ok(n, dtype_bytes(act), &n)) return 0;
-    return 2 * align256(n ? n : 1);
+    return 3 * align256(n ? n : 1);
 }
 
 moeq_status awq_swiglu_input_backward(const moeq_route *route, const void *values,
@@ -513,8 +516,9 @@ moeq_status awq_swiglu_input_backward(const moeq_route *route, const void *value
         return fail(MOEQ_EWORKSPACE, "workspace must be 256-byte aligned");
     if (workspace_bytes < need)
         return fail(MOEQ_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-    char *dg = static_cast<char *>(workspace);  // dh, then dG in place
-    char *du = dg + need / 2;
+    char *dh = static_cast<char *>(workspace);  // [A, I] each
+    char *gg = dh + need / 3;                   // G, then dG
+    char *uu = gg + need / 3;                   // U, then dU
     hipStream_t s = static_cast<hipStream_t>(stream);
     ProjProblem p{};
     p.offsets = route->expert_offsets;
@@ -523,42 +527,48 @@ moeq_status awq_swiglu_input_backward(const moeq_route *route, const void *value
     p.rows = A;
     p.E = route->E;
     p.act = act;
-    p.clamp = fn.clamp;
-    p.alpha = fn.alpha;
-    p.up_offset = fn.up_offset;
     // dh = grad . Wd^T
     ProjProblem q = p;
     q.in = grad;
-    q.out = dg;
+    q.out = dh;
     q.Kred = K;
     q.Nout = I;
-    q.w0 = operand_of(down);
-    q.w1 = q.w0;
+    q.w0 = q.w1 = operand_of(down);
     q.mode = PROJ_INPUT_VJP;
-    if ((st = device_status(launch_proj_generic(q, s), "down input VJP")) != MOEQ_OK) return st;
-    // G, U recomputed; dG over dh, dU
-    q = p;
-    q.in = values;
-    q.in2 = dg;
-    q.out = dg;
-    q.out2 = du;
-    q.Kred = K;
-    q.Nout = I;
-    q.w0 = operand_of(gate);
-    q.w1 = operand_of(up);
-    q.mode = PROJ_SWIGLU_VJP;
-    if ((st = device_status(launch_proj_generic(q, s), "SwiGLU VJP")) != MOEQ_OK) return st;
+    if ((st = device_status(vjp_fits(q) ? launch_vjp(q, s) : launch_proj_generic(q, s),
+                            "down input VJP")) != MOEQ_OK)
+        return st;
+    // G and U recomputed as in the forward (bias added, rounded to act)
+    for (int c = 0; c < 2; ++c) {
+        q = p;
+        q.in = values;
+        q.out = c == 0 ? gg : uu;
+        q.Kred = K;
+        q.Nout = I;
+        q.w0 = q.w1 = operand_of(c == 0 ? gate : up);
+        q.mode = PROJ_PLAIN;
+        bool handled = false;
+        hipError_t err = launch_fast_plain(q, s, &handled);
+        if (!handled) err = launch_proj_generic(q, s);
+        if ((st = device_status(err, "gate/up recompute")) != MOEQ_OK) return st;
+    }
+    // dG, dU in place of G, U
+    if ((st = device_status(launch_swiglu_vjp(gg, uu, dh, act, (size_t)A * I, fn.clamp, fn.alpha,
+                                              fn.up_offset, s),
+                            "SwiGLU VJP")) != MOEQ_OK)
+        return st;
     // grad_values = dG . Wg^T + dU . Wu^T
     q = p;
-    q.in = dg;
-    q.in2 = du;
+    q.in = gg;
+    q.in2 = uu;
     q.out = grad_values;
     q.Kred = I;
     q.Nout = K;
     q.w0 = operand_of(gate);
     q.w1 = operand_of(up);
     q.mode = PROJ_INPUT_VJP2;
-    return device_status(launch_proj_generic(q, s), "gate/up input VJP");
+    return device_status(vjp_fits(q) ? launch_vjp(q, s) : launch_proj_generic(q, s),
+                         "gate/up input VJP");
 }
 
 }  // extern "C"

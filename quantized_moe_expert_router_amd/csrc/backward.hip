@@ -135,7 +135,68 @@ __global__ __launch_bounds__(256) void weights_backward_kernel(
     }
 }
 
+// ------------------------------------------------------------------ SwiGLU VJP
+// Elementwise, in place: G becomes dG and U becomes dU, from dh and the
+// storage-rounded G, U of the recomputed gate/up projections:
+//   dG = dh (u' + off) (s + alpha g' s (1 - s)),  dU = dh g' s,  s = sigmoid(alpha g'),
+// g', u' the values clamped to [-clamp, clamp] when clamp > 0; a clamped value
+// passes the derivative on the closed interval and blocks it outside.  fp32
+// arithmetic, one rounding to the activation type per output.  For bf16 the
+// hardware exp and reciprocal (about one fp32 ulp each) stay far inside that
+// rounding; fp32 activations use the accurate library exp.
+template <int ACT>
+__global__ __launch_bounds__(256) void swiglu_vjp_kernel(void *__restrict__ G, void *__restrict__ U,
+                                                         const void *__restrict__ dh, size_t n,
+                                                         float clamp, float alpha, float off) {
+    typedef typename Storage<ACT>::T S;
+    constexpr int VEC = 16 / sizeof(S);
+    typedef S sv __attribute__((ext_vector_type(VEC)));
+    const size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * VEC;
+    if (i >= n) return;
+    sv *gp = reinterpret_cast<sv *>(static_cast<S *>(G) + i);
+    sv *up = reinterpret_cast<sv *>(static_cast<S *>(U) + i);
+    const sv gv = *gp, uv = *up;
+    const sv dv = *reinterpret_cast<const sv *>(static_cast<const S *>(dh) + i);
+    sv og, ou;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        float g = (float)gv[v], u = (float)uv[v];
+        const float d = (float)dv[v];
+        float gpass = 1.0f, upass = 1.0f;
+        if (clamp > 0.0f) {
+            gpass = (g >= -clamp && g <= clamp) ? 1.0f : 0.0f;
+            upass = (u >= -clamp && u <= clamp) ? 1.0f : 0.0f;
+            g = fminf(fmaxf(g, -clamp), clamp);
+            u = fminf(fmaxf(u, -clamp), clamp);
+        }
+        const float sg = ACT == MOEQ_F32 ? 1.0f / (1.0f + expf(-alpha * g))
+                                         : __builtin_amdgcn_rcpf(1.0f + __expf(-alpha * g));
+        og[v] = (S)(gpass * d * (u + off) * (sg + alpha * g * sg * (1.0f - sg)));
+        ou[v] = (S)(upass * d * g * sg);
+    }
+    *gp = og;
+    *up = ou;
+}
+
 }  // namespace
+
+hipError_t launch_swiglu_vjp(void *G, void *U, const void *dh, int act, size_t n, float clamp,
+                             float alpha, float up_offset, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const size_t vec = act == MOEQ_F32 ? 4 : 8;  // n % 8 == 0: whole vectors
+    const size_t threads = n / vec;
+    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    if (act == MOEQ_F32)
+        hipLaunchKernelGGL((swiglu_vjp_kernel<MOEQ_F32>), grid, block, 0, s, G, U, dh, n, clamp,
+                           alpha, up_offset);
+    else if (act == MOEQ_BF16)
+        hipLaunchKernelGGL((swiglu_vjp_kernel<MOEQ_BF16>), grid, block, 0, s, G, U, dh, n, clamp,
+                           alpha, up_offset);
+    else
+        hipLaunchKernelGGL((swiglu_vjp_kernel<MOEQ_F16>), grid, block, 0, s, G, U, dh, n, clamp,
+                           alpha, up_offset);
+    return hipGetLastError();
+}
 
 hipError_t launch_combine_backward(const void *y, int act, const float *weights,
                                    const int32_t *slot_pos, const void *grad, int T, int k, int K,

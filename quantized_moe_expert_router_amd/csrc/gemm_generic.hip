@@ -57,23 +57,6 @@ __device__ __forceinline__ float swiglu(float g, float u, float clamp, float alp
     return g * (1.0f / (1.0f + expf(-alpha * g))) * (u + off);
 }
 
-// Derivatives of h = g' sigmoid(alpha g') (u' + off) at the rounded G, U (g', u'
-// clamped when clamp > 0; a clamped value passes the derivative on the closed
-// interval and blocks it outside).
-__device__ __forceinline__ void swiglu_vjp(float g, float u, float d, float clamp, float alpha,
-                                           float off, float *dg, float *du) {
-    float gpass = 1.0f, upass = 1.0f;
-    if (clamp > 0.0f) {
-        gpass = (g >= -clamp && g <= clamp) ? 1.0f : 0.0f;
-        upass = (u >= -clamp && u <= clamp) ? 1.0f : 0.0f;
-        g = fminf(fmaxf(g, -clamp), clamp);
-        u = fminf(fmaxf(u, -clamp), clamp);
-    }
-    const float sg = 1.0f / (1.0f + expf(-alpha * g));
-    *dg = gpass * d * (u + off) * (sg + alpha * g * sg * (1.0f - sg));
-    *du = upass * d * g * sg;
-}
-
 template <int ACT, int SD, int MODE>
 __global__ __launch_bounds__(256) void proj_generic_kernel(ProjProblem p) {
     constexpr bool two_in = MODE == PROJ_INPUT_VJP2;
@@ -89,8 +72,7 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(ProjProblem p) {
     const int tid = threadIdx.x, cl = tid & (kCols - 1), rg = tid >> 6;
     const int col = blockIdx.x * kCols + cl;
     const bool col_ok = col < p.Nout;
-    const bool two = (MODE == PROJ_SWIGLU || MODE == PROJ_BANK_SWIGLU ||
-                      MODE == PROJ_SWIGLU_VJP || MODE == PROJ_INPUT_VJP2);
+    const bool two = (MODE == PROJ_SWIGLU || MODE == PROJ_BANK_SWIGLU || MODE == PROJ_INPUT_VJP2);
 
     for (int rc = r0; rc < r1; rc += kRowChunk) {
         float acc0[4] = {0.f, 0.f, 0.f, 0.f}, acc1[4] = {0.f, 0.f, 0.f, 0.f};
@@ -115,7 +97,7 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(ProjProblem p) {
                 if (MODE == PROJ_PLAIN) {
                     c0 = p.w0.format == MOEQ_FMT_AWQ ? awq_coeff<SD>(p.w0, e, kx, col)
                                                      : mxfp4_coeff(p.w0, e, col, kx);
-                } else if (MODE == PROJ_SWIGLU || MODE == PROJ_SWIGLU_VJP) {
+                } else if (MODE == PROJ_SWIGLU) {
                     c0 = awq_coeff<SD>(p.w0, e, kx, col);
                     c1 = awq_coeff<SD>(p.w1, e, kx, col);
                 } else if (MODE == PROJ_BANK_SWIGLU) {
@@ -154,14 +136,6 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(ProjProblem p) {
                 const float g = round_to<ACT>(acc0[i] + bias_value<SD>(p.w0, e, 2 * col));
                 const float u = round_to<ACT>(acc1[i] + bias_value<SD>(p.w0, e, 2 * col + 1));
                 v = swiglu(g, u, p.clamp, p.alpha, p.up_offset);
-            } else if (MODE == PROJ_SWIGLU_VJP) {
-                const size_t at = (size_t)row * p.Nout + col;
-                const float g = round_to<ACT>(acc0[i] + bias_value<SD>(p.w0, e, col));
-                const float u = round_to<ACT>(acc1[i] + bias_value<SD>(p.w1, e, col));
-                const float d = load_f<ACT>(p.in2, at);  // read before out (may alias) is written
-                float du;
-                swiglu_vjp(g, u, d, p.clamp, p.alpha, p.up_offset, &v, &du);
-                store_f<ACT>(p.out2, at, du);
             } else if (MODE == PROJ_INPUT_VJP2) {
                 v = acc0[i] + acc1[i];  // gate part, then up part
             } else {
@@ -184,10 +158,6 @@ hipError_t launch_mode(const ProjProblem &p, hipStream_t s) {
         break;
     case PROJ_BANK_SWIGLU:
         hipLaunchKernelGGL((proj_generic_kernel<ACT, SD, PROJ_BANK_SWIGLU>), grid, block, 0, s,
-                           p);
-        break;
-    case PROJ_SWIGLU_VJP:
-        hipLaunchKernelGGL((proj_generic_kernel<ACT, SD, PROJ_SWIGLU_VJP>), grid, block, 0, s,
                            p);
         break;
     case PROJ_INPUT_VJP2:

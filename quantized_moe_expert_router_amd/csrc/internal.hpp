@@ -32,8 +32,7 @@ struct PackedOperand {
 struct ProjProblem {
     const void *in;
     void *out;
-    const void *in2;     // second input: dh (SWIGLU_VJP) | dU (INPUT_VJP2)
-    void *out2;          // second output: dU (SWIGLU_VJP)
+    const void *in2;     // second input: dU (INPUT_VJP2)
     const int32_t *offsets;
     const int32_t *tile_offsets;  // [E+1] m-tile prefix (route), nullable
     const int32_t *tile_expert;   // expert of each m-tile (route), nullable
@@ -53,9 +52,7 @@ enum ProjMode {
     PROJ_SWIGLU = 1,     // out = SwiGLU(in . Wg (+ bg), in . Wu (+ bu)), AWQ
     PROJ_BANK_SWIGLU = 2,// MXFP4 interleaved gate/up bank + SwiGLU
     PROJ_INPUT_VJP = 3,  // out = in . W^T, AWQ (no bias)
-    PROJ_SWIGLU_VJP = 4, // G, U as in PROJ_SWIGLU; out = dG, out2 = dU from dh = in2
-                         // (out may alias in2: each element is read before written)
-    PROJ_INPUT_VJP2 = 5, // out = in . Wg^T + in2 . Wu^T, AWQ
+    PROJ_INPUT_VJP2 = 4, // out = in . Wg^T + in2 . Wu^T, AWQ
 };
 
 hipError_t launch_router(const float *logits, const float *bias, int T, int E, int k,
@@ -81,6 +78,10 @@ hipError_t launch_dispatch_backward(const void *grad, int act, const int32_t *sl
 hipError_t launch_combine_backward(const void *y, int act, const float *weights,
                                    const int32_t *slot_pos, const void *grad, int T, int k, int K,
                                    void *grad_y, float *grad_weights, hipStream_t s);
+hipError_t launch_swiglu_vjp(void *G, void *U, const void *dh, int act, size_t n, float clamp,
+                             float alpha, float up_offset, hipStream_t s);
+bool vjp_fits(const ProjProblem &p);
+hipError_t launch_vjp(const ProjProblem &p, hipStream_t s);
 hipError_t launch_weights_backward(const uint32_t *selected, const float *weights,
                                    const float *grad_weights, int T, int E, int k,
                                    float *grad_logits, hipStream_t s);

@@ -289,13 +289,18 @@ def awq_input_backward(route: Optional[RouteState], grad: torch.Tensor, w: AwqEx
 
 # ------------------------------------------------------------------ backward path
 def moe_combine_backward(route: RouteState, y: torch.Tensor, weights: torch.Tensor,
-                         grad: torch.Tensor, experts: bool = True, want_weights: bool = True):
+                         grad: torch.Tensor, experts: bool = True, want_weights: bool = True,
+                         grad_y: Optional[torch.Tensor] = None,
+                         grad_weights: Optional[torch.Tensor] = None):
     """Combine VJP with a MoeCombineSelection: (grad_y [A,K] or None,
     grad_weights [T,top_k] fp32 or None); only the requested ones are formed."""
     K = y.shape[1]
-    gy = torch.empty_like(y) if experts else None
-    gw = (torch.empty(route.T, route.top_k, dtype=torch.float32, device=y.device)
-          if want_weights else None)
+    gy = gw = None
+    if experts:
+        gy = torch.empty_like(y) if grad_y is None else grad_y
+    if want_weights:
+        gw = (torch.empty(route.T, route.top_k, dtype=torch.float32, device=y.device)
+              if grad_weights is None else grad_weights)
     _check(lib().moe_combine_backward(C.byref(route.c), _ptr(y), _dt(y), K, _ptr(weights),
                                       _ptr(grad), _ptr(gy), _ptr(gw), _stream(y.device)))
     return gy, gw

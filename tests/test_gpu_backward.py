@@ -189,3 +189,41 @@ def test_backward_no_tokens():
     assert moeq.moe_dispatch_weights_backward(r, disp["selected"], disp["weights"],
                                               disp["weights"]).shape == (0, 8)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T,E,k,H,I,g,sdt,skew", [
+    (600, 8, 2, 512, 320, 64, "bf16", False),   # 128-row kernel, idle column waves
+    (600, 8, 2, 512, 320, 32, "f16", False),    # two groups per 64 columns
+    (700, 6, 3, 384, 256, 128, "f32", True),    # fp32 scales, one heavy expert
+    (40, 4, 2, 256, 192, 64, "bf16", True),     # streaming kernel, several 16-row passes
+    (50, 16, 4, 320, 128, 32, "f32", False),    # streaming kernel, g = 32, fp32 scales
+])
+def test_input_vjp_kernel_paths(T, E, k, H, I, g, sdt, skew):
+    """Both cubes' input VJPs and the chain across the MFMA kernels' shape cases."""
+    print(f"[input vjp paths] T={T} E={E} k={k} H={H} I={I} g={g} {sdt} skew={skew}", flush=True)
+    cfg = dataclasses.replace(CONFIGS["decode"], T=T, E=E, k=k, H=H, I=I, group=g, sdt=sdt,
+                              awq_bias=True)
+    p = make_inputs(cfg, seed=48)
+    if skew:
+        p["router_bias"] = np.zeros(E, np.float32)
+        p["router_bias"][1] = 4.0                  # expert 1 takes nearly every token
+    d = di.upload(p, DEV)
+    disp = moeq.moe_dispatch(d["x"], d["logits"], d["router_bias"], k)
+    sel, _ = oracle.route(p["logits"], p["router_bias"], k)
+    _, src, _, rex = oracle.dispatch_index(sel, E)
+    A = T * k
+    rng = np.random.default_rng(49)
+    for name, N in (("gate", I), ("down", H)):
+        grad = to_storage(rng.normal(0, 1, (A, N)), "bf16")
+        gi = moeq.awq_input_backward(disp["route"], di.tensor(grad, "bf16", DEV), d[name])
+        torch.cuda.synchronize()
+        ref = oracle.awq_input_backward(grad, "bf16", rex, p[name + "_qw"], p[name + "_qz"],
+                                        p[name + "_s"], sdt, g)
+        assert row_rel_err(f64(di.to_host(gi, "bf16"), "bf16"), f64(ref, "bf16")) <= TOL["bf16"]
+    grad = to_storage(rng.normal(0, 1, (A, H)), "bf16")
+    gv = moeq.awq_swiglu_input_backward(disp["route"], disp["values"], d["gate"], d["up"],
+                                        d["down"], di.tensor(grad, "bf16", DEV))
+    torch.cuda.synchronize()
+    values = oracle.copy_rows(p["x"], src)
+    ref = chain_reference(p, values, grad, rex, np.arange(A), (0.0, 1.0, 0.0))
+    assert row_rel_err(f64(di.to_host(gv, "bf16"), "bf16"), f64(ref, "bf16")) <= TOL["bf16"]
