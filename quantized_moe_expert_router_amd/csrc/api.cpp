@@ -538,8 +538,27 @@ moeq_status awq_swiglu_input_backward(const moeq_route *route, const void *value
     if ((st = device_status(vjp_fits(q) ? launch_vjp(q, s) : launch_proj_generic(q, s),
                             "down input VJP")) != MOEQ_OK)
         return st;
-    // G and U recomputed as in the forward (bias added, rounded to act)
-    for (int c = 0; c < 2; ++c) {
+    // G and U recomputed as in the forward (bias added, rounded to act), with the
+    // SwiGLU VJP in the gate/up kernel's epilogue: dG, dU straight from dh
+    q = p;
+    q.in = values;
+    q.in2 = dh;
+    q.out = gg;
+    q.out2 = uu;
+    q.Kred = K;
+    q.Nout = I;
+    q.w0 = operand_of(gate);
+    q.w1 = operand_of(up);
+    q.mode = PROJ_SWIGLU;
+    q.clamp = fn.clamp;
+    q.alpha = fn.alpha;
+    q.up_offset = fn.up_offset;
+    bool fused = false;
+    if ((st = device_status(launch_fast_swiglu(q, s, &fused), "gate/up backward epilogue")) !=
+        MOEQ_OK)
+        return st;
+    // otherwise: G and U by two plain projections, then the SwiGLU VJP in place
+    for (int c = 0; c < 2 && !fused; ++c) {
         q = p;
         q.in = values;
         q.out = c == 0 ? gg : uu;
@@ -552,8 +571,8 @@ moeq_status awq_swiglu_input_backward(const moeq_route *route, const void *value
         if (!handled) err = launch_proj_generic(q, s);
         if ((st = device_status(err, "gate/up recompute")) != MOEQ_OK) return st;
     }
-    // dG, dU in place of G, U
-    if ((st = device_status(launch_swiglu_vjp(gg, uu, dh, act, (size_t)A * I, fn.clamp, fn.alpha,
+    if (!fused &&
+        (st = device_status(launch_swiglu_vjp(gg, uu, dh, act, (size_t)A * I, fn.clamp, fn.alpha,
                                               fn.up_offset, s),
                             "SwiGLU VJP")) != MOEQ_OK)
         return st;

@@ -73,6 +73,24 @@ __device__ __forceinline__ float swiglu_f(float g, float u, float clamp, float a
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-alpha * g)) * (u + off);
 }
 
+// Derivatives of h = g' sigmoid(alpha g') (u' + off) for the backward epilogues
+// (bf16 outputs; hardware exp and reciprocal as in swiglu_f): g', u' clamped
+// when clamp > 0, a clamped value passing the derivative on the closed interval
+// and blocking it outside.
+__device__ __forceinline__ void swiglu_vjp_f(float g, float u, float d, float clamp, float alpha,
+                                             float off, float *dg, float *du) {
+    float gpass = 1.0f, upass = 1.0f;
+    if (clamp > 0.0f) {
+        gpass = (g >= -clamp && g <= clamp) ? 1.0f : 0.0f;
+        upass = (u >= -clamp && u <= clamp) ? 1.0f : 0.0f;
+        g = fminf(fmaxf(g, -clamp), clamp);
+        u = fminf(fmaxf(u, -clamp), clamp);
+    }
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-alpha * g));
+    *dg = gpass * d * (u + off) * (sg + alpha * g * sg * (1.0f - sg));
+    *du = upass * d * g * sg;
+}
+
 // Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
 // only.  __syncthreads() also waits for every global load in flight
 // (vmcnt(0)), which would drain the prefetch ring at each barrier.  The

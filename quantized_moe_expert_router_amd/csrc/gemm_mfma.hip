@@ -52,6 +52,8 @@ struct StreamArgs {
     const void *sc[2];
     const void *bias[2];
     float clamp, alpha, up_offset;
+    const __bf16 *dh;  // backward epilogue: [A, N] derivative of h (NULL: forward)
+    __bf16 *out2;      // backward epilogue: dU (out holds dG)
 };
 
 // ------------------------------------------------------------------ stream
@@ -80,7 +82,7 @@ constexpr int stream_lds_bufs() {
     return tree > join ? tree : (join > 0 ? join : 1);
 }
 
-template <int NSETS, int SD, int SPW, int KSPLIT, int RT, int DEPTH, int SPG>
+template <int NSETS, int SD, int SPW, int KSPLIT, int RT, int DEPTH, int SPG, bool BWD>
 __global__ __launch_bounds__(64 * NSETS * SPW * KSPLIT)
 __attribute__((amdgpu_waves_per_eu(stream_waves<RT>(), stream_waves<RT>())))
 void awq_stream_kernel(StreamArgs a) {
@@ -319,6 +321,15 @@ void awq_stream_kernel(StreamArgs a) {
                         if (NSETS == 2) {
                             const float gv = round_to<MOEQ_BF16>(acc[sl][rt][i] + b0);
                             const float uv = round_to<MOEQ_BF16>(up4[i] + b1);
+                            if constexpr (BWD) {  // backward: dG, dU at the rounded G, U
+                                const size_t at = (size_t)row * N + col;
+                                float dg, du;
+                                swiglu_vjp_f(gv, uv, (float)a.dh[at], a.clamp, a.alpha,
+                                             a.up_offset, &dg, &du);
+                                a.out[at] = (__bf16)dg;
+                                a.out2[at] = (__bf16)du;
+                                continue;
+                            }
                             v = swiglu_f(gv, uv, a.clamp, a.alpha, a.up_offset);
                         } else {
                             v = acc[sl][rt][i] + b0;
@@ -331,13 +342,13 @@ void awq_stream_kernel(StreamArgs a) {
     }
 }
 
-template <int NSETS, int SD, int SPW>
+template <int NSETS, int SD, int SPW, bool BWD>
 hipError_t launch_stream(const StreamArgs &a, int E, int ksplit, int rt, int depth,
                          hipStream_t s) {
     dim3 grid(a.xcd_pairs ? ((E + 7) / 8) * 8 * a.parts : E * a.parts);
 #define MOEQ_STREAM(KS, RTT, D, SP)                                                          \
     if (ksplit == KS && rt == RTT && depth == D) {                                           \
-        hipLaunchKernelGGL((awq_stream_kernel<NSETS, SD, SPW, KS, RTT, D, SP>), grid,        \
+        hipLaunchKernelGGL((awq_stream_kernel<NSETS, SD, SPW, KS, RTT, D, SP, BWD>), grid,   \
                            dim3(64 * NSETS * SPW * KS), 0, s, a);                            \
         return hipGetLastError();                                                            \
     }
@@ -352,6 +363,25 @@ hipError_t launch_stream(const StreamArgs &a, int E, int ksplit, int rt, int dep
     MOEQ_STREAM(1, 2, 1, 0)
 #undef MOEQ_STREAM
     return hipErrorInvalidValue;
+}
+
+template <int NSETS, int SPW, bool BWD>
+hipError_t stream_by_sdt_b(const StreamArgs &a, int sdt, int E, int ksplit, int rt, int depth,
+                           hipStream_t s) {
+    switch (sdt) {
+    case MOEQ_BF16: return launch_stream<NSETS, MOEQ_BF16, SPW, BWD>(a, E, ksplit, rt, depth, s);
+    case MOEQ_F16: return launch_stream<NSETS, MOEQ_F16, SPW, BWD>(a, E, ksplit, rt, depth, s);
+    default: return launch_stream<NSETS, MOEQ_F32, SPW, BWD>(a, E, ksplit, rt, depth, s);
+    }
+}
+
+// the backward epilogue is a separate instantiation: the forward kernels stay as they are
+template <int NSETS, int SPW>
+hipError_t stream_by_sdt(const StreamArgs &a, int sdt, int E, int ksplit, int rt, int depth,
+                         hipStream_t s) {
+    if constexpr (NSETS == 2)
+        if (a.dh) return stream_by_sdt_b<NSETS, SPW, true>(a, sdt, E, ksplit, rt, depth, s);
+    return stream_by_sdt_b<NSETS, SPW, false>(a, sdt, E, ksplit, rt, depth, s);
 }
 
 // Host-side choice of the stream kernel for a bf16 AWQ projection.
@@ -384,6 +414,8 @@ hipError_t run_stream(const ProjProblem &p, hipStream_t s) {
     a.clamp = p.clamp;
     a.alpha = p.alpha;
     a.up_offset = p.up_offset;
+    a.dh = static_cast<const __bf16 *>(p.in2);
+    a.out2 = static_cast<__bf16 *>(p.out2);
     const int strips = a.W / 16;
     // rows: one 16-row tile unless experts average more than 8 rows
     const int rt = ((double)p.rows / (double)p.E) <= 8.0 ? 1 : 2;
@@ -417,13 +449,8 @@ hipError_t run_stream(const ProjProblem &p, hipStream_t s) {
     a.E = p.E;
     a.xcd_pairs = 1;
     if (const char *v = getenv("MOEQ_STREAM_XCD")) a.xcd_pairs = atoi(v) != 0;
-#define MOEQ_SPW(X)                                                                             \
-    case X:                                                                                     \
-        switch (p.w0.sdt) {                                                                     \
-        case MOEQ_BF16: return launch_stream<NSETS, MOEQ_BF16, X>(a, p.E, ksplit, rt, depth, s); \
-        case MOEQ_F16: return launch_stream<NSETS, MOEQ_F16, X>(a, p.E, ksplit, rt, depth, s);   \
-        default: return launch_stream<NSETS, MOEQ_F32, X>(a, p.E, ksplit, rt, depth, s);         \
-        }
+#define MOEQ_SPW(X) \
+    case X: return stream_by_sdt<NSETS, X>(a, p.w0.sdt, p.E, ksplit, rt, depth, s);
     switch (spw) {
         MOEQ_SPW(1)
         MOEQ_SPW(2)
@@ -465,6 +492,7 @@ hipError_t launch_fast_swiglu(const ProjProblem &p, hipStream_t s, bool *handled
         *handled = true;
         return launch_ws(p, s);
     }
+    if (p.in2) return hipSuccess;  // the backward epilogue lives in the three kernels above
     if (p.tile_offsets && tile_fits(p)) {
         *handled = true;
         return launch_tile(p, p.tile_offsets, p.tile_expert, s);

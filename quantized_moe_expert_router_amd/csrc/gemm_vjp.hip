@@ -19,21 +19,24 @@
 //
 // Each wave owns 64 output columns (four 16-column tiles) and RT 16-row tiles,
 // and reuses every decoded B operand for RT MFMAs.
-//  RT = 8 (many rows per expert): one block = one 128-row m-tile of the route
-//   x CG waves of columns; the 128 x 64 bf16 A slab of a step is staged in a
+//  RT = 8 (more than 8 rows per expert on average): one block = one 128-row
+//   m-tile of the route x CG waves of columns, doing only the row tiles that
+//   hold rows; the 128 x 64 bf16 A slab of a step is staged in a
 //   double-buffered LDS tile of 128-byte rows whose 16-byte chunks are permuted
 //   by chunk ^ ((row >> 1) & 7), so that the fragment reads of 16 rows x one
 //   chunk and the row-wise stores are both free of bank conflicts; one
 //   LDS-only barrier per step.
-//  RT = 1 (few rows per expert, decode): the block walks its m-tile 16 rows at
-//   a time and each wave reads its A fragments straight from memory; weight
-//   words, zeros, scales and A run DEPTH steps ahead in registers, so the
-//   kernel streams the cubes at HBM rate.
+//  RT = 1 (few rows per expert, decode): a block is 64 columns of one m-tile,
+//   its waves split the reduction; it walks the m-tile 16 rows at a time,
+//   staging those rows in LDS; weight words, zeros and scales run DEPTH steps
+//   of 256 reduction elements ahead in registers, each load reading whole
+//   128-byte lines of a weight row.
 // Blocks deal m-tiles to the eight XCDs in contiguous ranges (block b runs on
 // XCD b % 8): the column blocks of an m-tile and the m-tiles of one expert
 // share that XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
 #include <cstdlib>
 
 #include "awq_dequant.hpp"
@@ -175,6 +178,7 @@ void awq_vjp_tile_kernel(VjpArgs a) {
     const bool active = k0 < a.Kout;  // idle waves still stage A and meet every barrier
     const int kb = active ? k0 : 0;
     const int S = NSETS * a.Nred / kStepN, spn = a.Nred / kStepN;
+    const int rtn = (m1 - m0 + 15) >> 4;  // row tiles holding rows (block-uniform)
 
     // cooperative staging: chunk ci = tid + kThreads * j -> (row ci / 8, chunk ci % 8)
     const int tid = threadIdx.x;
@@ -217,6 +221,7 @@ void awq_vjp_tile_kernel(VjpArgs a) {
             build_b<SD, NG>(bcur, t, B);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
+                if (rt >= rtn) break;  // a partly filled m-tile does only its row tiles
                 const int row = rt * 16 + c, ch = 2 * q + t;
                 const bf16x8 A = *reinterpret_cast<const bf16x8 *>(
                     &sl[row * kStepN + 8 * (ch ^ ((row >> 1) & 7))]);
@@ -239,80 +244,241 @@ void awq_vjp_tile_kernel(VjpArgs a) {
 }
 
 // ------------------------------------------------------------------ RT = 1
+// Steps of 256 reduction elements: lane group q takes the eight words
+// 8q..8q+7 of each of its rows (32 contiguous bytes, so the four lane groups
+// read whole 128-byte lines of a weight row) and the eight MFMA sub-steps t
+// use word 8q + t.  The block's (at most 16) gradient rows are staged once per
+// pass in LDS (16 rows x all reduction elements of both cubes), with 16-byte
+// chunks permuted by chunk ^ row so that a fragment read of 16 rows x one chunk
+// is free of bank conflicts.
+constexpr int kStreamStep = 256;
+constexpr size_t kStreamLds = 64 * 1024;  // staged rows: 16 x (reduction of both cubes) bf16
+
 template <int SD, int NG>
-struct StepAB {
-    StepB<SD, NG> b;
-    u32x4 a[2];  // A fragments of the two sub-steps
+struct StreamB {
+    static constexpr int kSv = SD == MOEQ_F32 ? 16 : 8;  // 16-byte scale vectors (64 scales)
+    u32x4 w[4][2];   // words 8q..8q+7 of each column tile's row
+    u32x4 z[NG][2];  // zero words 8q..8q+7
+    u32x4 s[NG][kSv];
 };
 
-template <int NSETS, int SD, int NG, int CG, int DEPTH>
-__global__ __launch_bounds__(64 * CG)
+template <int SD, int NG>
+__device__ __forceinline__ void load_stream_b(const VjpArgs &a, int e, int k0, int q, int c,
+                                              int st, StreamB<SD, NG> &b) {
+    constexpr int sb = SD == MOEQ_F32 ? 4 : 2;
+    const int spn = a.Nred / kStreamStep;
+    const int set = st >= spn ? 1 : 0;
+    const int n0 = (st - set * spn) * kStreamStep;
+    const int Wn = a.Nred >> 3, G = a.Kout / a.g;
+    const int wi = (n0 >> 3) + 8 * q;
+    const uint32_t *qw = a.qw[set] + (size_t)e * a.Kout * Wn + wi;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(qw + (size_t)(k0 + 16 * ct + c) * Wn);
+        b.w[ct][0] = p[0];
+        b.w[ct][1] = p[1];
+    }
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        const size_t gr = (size_t)e * G + (k0 + gi * (64 / NG)) / a.g;
+        const u32x4 *zp = reinterpret_cast<const u32x4 *>(a.qz[set] + gr * Wn + wi);
+        b.z[gi][0] = zp[0];
+        b.z[gi][1] = zp[1];
+        const u32x4 *sp = reinterpret_cast<const u32x4 *>(
+            static_cast<const char *>(a.sc[set]) + (gr * a.Nred + n0 + 64 * q) * sb);
+#pragma unroll
+        for (int v = 0; v < StreamB<SD, NG>::kSv; ++v) b.s[gi][v] = sp[v];
+    }
+}
+
+// B operands of sub-step t (word 8q + t) for the four column tiles, in n order.
+template <int SD, int NG>
+__device__ __forceinline__ void build_stream_b(const StreamB<SD, NG> &b, int t, bf16x8 B[4]) {
+    GroupConst<SD> gc[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        GroupRaw<SD> r;
+        r.zw = b.z[gi][t >> 2][t & 3];
+        if (SD == MOEQ_F32) {
+            r.s0 = b.s[gi][2 * t];
+            r.s1 = b.s[gi][(2 * t + 1) % StreamB<SD, NG>::kSv];
+        } else {
+            r.s0 = b.s[gi][t];
+        }
+        decode_group<SD>(r, gc[gi]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        const GroupConst<SD> &g = gc[NG == 1 ? 0 : ct / 2];
+        float qv[8], cf[8];
+        decode_codes(b.w[ct][t >> 2][t & 3], qv);
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) cf[sl] = coeff<SD>(qv[sl], g, sl);
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = pack_bf16(cf[kColSlot[2 * i]], cf[kColSlot[2 * i + 1]]);
+        B[ct] = __builtin_bit_cast(bf16x8, v);
+    }
+}
+
+// Block = CG groups of 64 output columns x KS waves each; wave (cg, ks)
+// reduces the contiguous step range [ks S / KS, (ks + 1) S / KS), and the KS
+// partial sums of a column group meet in LDS (reusing the staging buffer) in
+// a fixed order.
+template <int NSETS, int SD, int NG, int CG, int KS, int DEPTH>
+__global__ __launch_bounds__(64 * CG * KS)
 void awq_vjp_stream_kernel(VjpArgs a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char vjp_lds[];
+    __bf16 *As = reinterpret_cast<__bf16 *>(vjp_lds);  // [16][NSETS * Nred], chunk-permuted
+    f32x4 *red = reinterpret_cast<f32x4 *>(vjp_lds);    // [CG][KS - 1][4][64] after the loop
     int mt, nb;
     bool ok;
     block_to_tile(a, &mt, &nb, &ok);
     if (!ok) return;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int k0 = (nb * CG + wv) * 64;
-    if (k0 >= a.Kout) return;  // no barriers in this kernel
+    const int cg = wv % CG, ks = wv / CG;
+    const int k0 = (nb * CG + cg) * 64;
+    const bool active = k0 < a.Kout;  // idle waves still stage rows and meet every barrier
+    const int kb = active ? k0 : 0;
     const int e = a.tile_expert[mt];
     const int m0 = a.offsets[e] + (mt - a.tile_offsets[e]) * kMTile;
     const int m1 = min(m0 + kMTile, a.offsets[e + 1]);
     const int lane = threadIdx.x & 63, c = lane & 15, q = lane >> 4;
-    const int S = NSETS * a.Nred / kStepN, spn = a.Nred / kStepN;
+    const int Ntot = NSETS * a.Nred, cpr = Ntot >> 3;  // 16-byte chunks per staged row
+    const int S = Ntot / kStreamStep, per = S / KS, sbeg = ks * per;
 
     for (int r0 = m0; r0 < m1; r0 += 16) {
-        const int arow = min(r0 + c, m1 - 1);  // rows past the tile repeat the last row
-        auto load = [&](int st, StepAB<SD, NG> &d) {
-            load_step_b<SD, NG>(a, e, k0, q, c, st, d.b);
-            const int set = st >= spn ? 1 : 0;
-            const int n0 = (st - set * spn) * kStepN;
-            const u32x4 *ap =
-                reinterpret_cast<const u32x4 *>(a.in[set] + (size_t)arow * a.Nred + n0 + 16 * q);
-            d.a[0] = ap[0];
-            d.a[1] = ap[1];
-        };
         f32x4 acc[4];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        StepAB<SD, NG> ring[DEPTH];
+        // stage the pass's rows, eight loads in flight per thread (indices past
+        // the end repeat the last chunk); fragment reads of rows past the last
+        // one read the last row, whose results land in rows that are not stored
+        const int nrows = min(16, m1 - r0), arow = min(c, nrows - 1);
+        const int total = nrows * cpr;
+        for (int i0 = threadIdx.x; i0 < total; i0 += 8 * blockDim.x) {
+            u32x4 v[8];
+            int at[8];
 #pragma unroll
-        for (int d = 0; d < DEPTH; ++d) load(min(d, S - 1), ring[d]);
-        for (int s0 = 0; s0 < S; s0 += DEPTH) {
+            for (int j = 0; j < 8; ++j) {
+                const int i = min(i0 + j * (int)blockDim.x, total - 1);
+                const int r = i / cpr, ch = i - r * cpr;
+                const int row = r0 + r;
+                const int n = ch * 8, set = n >= a.Nred ? 1 : 0;
+                v[j] = *reinterpret_cast<const u32x4 *>(a.in[set] + (size_t)row * a.Nred +
+                                                        (n - set * a.Nred));
+                at[j] = r * Ntot + 8 * (ch ^ r);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4 *>(As + at[j]) = v[j];
+        }
+        // per % DEPTH == 0 (chosen on the host): the loop body has no branches,
+        // so the wait before each use counts exactly the DEPTH - 1 younger steps.
+        StreamB<SD, NG> ring[DEPTH];
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            load_stream_b<SD, NG>(a, e, kb, q, c, sbeg + d, ring[d]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        for (int s0 = 0; s0 < per; s0 += DEPTH) {
 #pragma unroll
             for (int d = 0; d < DEPTH; ++d) {
-                if (s0 + d < S) {
+                const int chb = ((sbeg + s0 + d) * kStreamStep >> 3) + 8 * q;
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        bf16x8 B[4];
-                        build_b<SD, NG>(ring[d].b, t, B);
-                        const bf16x8 A = __builtin_bit_cast(bf16x8, ring[d].a[t]);
+                for (int t = 0; t < 8; ++t) {
+                    bf16x8 B[4];
+                    build_stream_b<SD, NG>(ring[d], t, B);
+                    const bf16x8 A = *reinterpret_cast<const bf16x8 *>(
+                        As + (size_t)arow * Ntot + 8 * ((chb + t) ^ arow));
 #pragma unroll
-                        for (int ct = 0; ct < 4; ++ct)
-                            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[ct], acc[ct],
-                                                                              0, 0, 0);
-                    }
+                    for (int ct = 0; ct < 4; ++ct)
+                        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B[ct], acc[ct], 0,
+                                                                          0, 0);
                 }
-                load(min(s0 + d + DEPTH, S - 1), ring[d]);
+                // past the range: a harmless reload of its last step
+                load_stream_b<SD, NG>(a, e, kb, q, c, sbeg + min(s0 + d + DEPTH, per - 1),
+                                      ring[d]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+        if constexpr (KS > 1) {
+            __syncthreads();  // every wave is done with the staged rows
+            if (ks > 0) {
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) store_tile(a, acc[ct], r0, m1, k0 + 16 * ct + c, lane);
+                for (int ct = 0; ct < 4; ++ct)
+                    red[((cg * (KS - 1) + ks - 1) * 4 + ct) * 64 + lane] = acc[ct];
+            }
+            __syncthreads();
+            if (ks == 0) {
+#pragma unroll
+                for (int w = 1; w < KS; ++w)
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+                        acc[ct] += red[((cg * (KS - 1) + w - 1) * 4 + ct) * 64 + lane];
+            }
+        }
+        if (ks == 0 && active) {
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) store_tile(a, acc[ct], r0, m1, k0 + 16 * ct + c, lane);
+        }
+        __syncthreads();  // the next pass restages the rows
     }
+}
+
+template <int NSETS, int SD, int NG, int CG, int KS>
+hipError_t launch_stream_ks(const VjpArgs &a, int per, int per_xcd, size_t lds, hipStream_t s) {
+    VjpArgs b = a;
+    b.nblk = (a.Kout / 64 + CG - 1) / CG;
+    const dim3 grid(8 * per_xcd * b.nblk), block(64 * CG * KS);
+    if (per % 2 == 0)
+        hipLaunchKernelGGL((awq_vjp_stream_kernel<NSETS, SD, NG, CG, KS, 2>), grid, block, lds, s,
+                           b);
+    else
+        hipLaunchKernelGGL((awq_vjp_stream_kernel<NSETS, SD, NG, CG, KS, 1>), grid, block, lds, s,
+                           b);
+    return hipGetLastError();
 }
 
 template <int NSETS, int SD, int NG>
 hipError_t launch_nsets(const VjpArgs &a, bool many, int max_tiles, hipStream_t s) {
-    constexpr int CG = 4;
-    VjpArgs b = a;
-    b.nblk = (a.Kout / 64 + CG - 1) / CG;
     const int per_xcd = (max_tiles + 7) / 8;
-    const dim3 grid(8 * per_xcd * b.nblk), block(64 * CG);
-    if (many)
+    const int S = NSETS * a.Nred / kStreamStep;
+    const size_t lds = (size_t)16 * NSETS * a.Nred * 2;
+    if (many || a.Nred % kStreamStep != 0 || lds > kStreamLds) {
+        constexpr int CG = 4;
+        VjpArgs b = a;
+        b.nblk = (a.Kout / 64 + CG - 1) / CG;
+        const dim3 grid(8 * per_xcd * b.nblk), block(64 * CG);
         hipLaunchKernelGGL((awq_vjp_tile_kernel<NSETS, SD, NG, CG>), grid, block, 0, s, b);
-    else
-        hipLaunchKernelGGL((awq_vjp_stream_kernel<NSETS, SD, NG, CG, 4>), grid, block, 0, s, b);
-    return hipGetLastError();
+        return hipGetLastError();
+    }
+    // launch shape: CG column groups x KS reduction slices per block
+    int cg = 4, ks = 1;
+    if (const char *v = getenv("MOEQ_VJP_SHAPE")) {  // tuning override "CGxKS" (shape only)
+        int x = 0, y = 0;
+        if (sscanf(v, "%dx%d", &x, &y) == 2 && (x == 1 || x == 2 || x == 4 || x == 8) &&
+            (y == 1 || y == 2 || y == 3 || y == 4) && S % y == 0) {
+            cg = x;
+            ks = y;
+        }
+    }
+    const int per = S / ks;
+#define MOEQ_VJP_SHAPE(X, Y) \
+    if (cg == X && ks == Y) return launch_stream_ks<NSETS, SD, NG, X, Y>(a, per, per_xcd, lds, s);
+    MOEQ_VJP_SHAPE(4, 1)
+    MOEQ_VJP_SHAPE(2, 1)
+    MOEQ_VJP_SHAPE(1, 1)
+    MOEQ_VJP_SHAPE(2, 2)
+    MOEQ_VJP_SHAPE(1, 2)
+    MOEQ_VJP_SHAPE(1, 3)
+    MOEQ_VJP_SHAPE(1, 4)
+    MOEQ_VJP_SHAPE(2, 4)
+    MOEQ_VJP_SHAPE(4, 2)
+    MOEQ_VJP_SHAPE(2, 3)
+    MOEQ_VJP_SHAPE(8, 1)
+#undef MOEQ_VJP_SHAPE
+    return launch_stream_ks<NSETS, SD, NG, 4, 1>(a, S, per_xcd, lds, s);
 }
 
 template <int NSETS, int SD>
@@ -373,8 +539,8 @@ hipError_t launch_vjp(const ProjProblem &p, hipStream_t s) {
     a.sc[0] = p.w0.scales;
     a.sc[1] = w1.scales;
     const int max_tiles = (p.rows + kMTile - 1) / kMTile + p.E;
-    // many rows per expert on average: the LDS-staged 128-row kernel
-    const bool many = (long)p.rows >= 32L * p.E;
+    // more than a few rows per expert on average: the LDS-staged 128-row kernel
+    const bool many = (long)p.rows > 8L * p.E;
     return two ? launch_ns<2>(a, p.w0.sdt, many, max_tiles, s)
                : launch_ns<1>(a, p.w0.sdt, many, max_tiles, s);
 }

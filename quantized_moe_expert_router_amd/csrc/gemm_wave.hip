@@ -69,6 +69,8 @@ struct WaveArgs {
     const void *sc[2];
     const void *bias[2];
     float clamp, alpha, up_offset;
+    const __bf16 *dh;  // backward epilogue: [A, Nout] derivative of h (NULL: forward)
+    __bf16 *out2;      // backward epilogue: dU (out holds dG)
 };
 
 template <int NSETS>
@@ -253,6 +255,49 @@ void awq_wave_kernel(WaveArgs a) {
         }
         __syncthreads();
         if (!active || set == 1) return;
+        if (a.dh) {
+            // backward: dG into out, dU into out2, at the rounded G, U.  The dh pair
+            // at col0 holds slots (0, 2), the pair at col0 + 4 slots (1, 3).
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                if (rt >= rtn) continue;
+                float gvv[4][4], uvv[4][4];  // [slot][row i]
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const uint2 u = lds.U[pair][s4 * RT + rt][lane];
+                    uvv[s4][0] = __uint_as_float(u.x << 16);
+                    uvv[s4][1] = __uint_as_float(u.x & 0xFFFF0000u);
+                    uvv[s4][2] = __uint_as_float(u.y << 16);
+                    uvv[s4][3] = __uint_as_float(u.y & 0xFFFF0000u);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        gvv[s4][i] = round_to<MOEQ_BF16>(acc[s4][rt][i] + bias_v[s4]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = m0 + rt * 16 + grp * 4 + i;
+                    if (row >= m1) continue;
+                    const size_t at = (size_t)row * a.Nout + col0;
+                    const uint32_t *dp = reinterpret_cast<const uint32_t *>(a.dh + at);
+                    const uint32_t d02 = dp[0], d13 = dp[2];
+                    const float dv[4] = {__uint_as_float(d02 << 16), __uint_as_float(d13 << 16),
+                                         __uint_as_float(d02 & 0xFFFF0000u),
+                                         __uint_as_float(d13 & 0xFFFF0000u)};
+                    float dg[4], du[4];
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4)
+                        swiglu_vjp_f(gvv[s4][i], uvv[s4][i], dv[s4], a.clamp, a.alpha,
+                                     a.up_offset, &dg[s4], &du[s4]);
+                    uint32_t *o = reinterpret_cast<uint32_t *>(a.out + at);
+                    uint32_t *o2 = reinterpret_cast<uint32_t *>(a.out2 + at);
+                    o[0] = pack_bf16(dg[0], dg[2]);
+                    o[2] = pack_bf16(dg[1], dg[3]);
+                    o2[0] = pack_bf16(du[0], du[2]);
+                    o2[2] = pack_bf16(du[1], du[3]);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             if (rt >= rtn) continue;
@@ -323,6 +368,8 @@ hipError_t run_wave(const ProjProblem &p, hipStream_t s) {
     a.clamp = p.clamp;
     a.alpha = p.alpha;
     a.up_offset = p.up_offset;
+    a.dh = static_cast<const __bf16 *>(p.in2);
+    a.out2 = static_cast<__bf16 *>(p.out2);
     // m-tiles are at most ceil(A / 128) + E; blocks past the last tile exit
     const long mtiles = ((long)p.rows + kWaveRows - 1) / kWaveRows + p.E;
     const long blocks = 8 * ((mtiles + 7) / 8) * a.nblk;

@@ -68,6 +68,8 @@ struct WsArgs {
     const void *sc[2];
     const void *bias[2];
     float clamp, alpha, up_offset;
+    const __bf16 *dh;  // backward epilogue: [A, Nout] derivative of h (NULL: forward)
+    __bf16 *out2;      // backward epilogue: dU (out holds dG)
 };
 
 __device__ __forceinline__ int lds_chunk(int row, int ch) { return ch ^ ((row >> 1) & 3); }
@@ -308,6 +310,15 @@ void awq_ws_kernel(WsArgs a) {
                 if (NSETS == 2) {
                     const float gv = round_to<MOEQ_BF16>(acc[rt][t][i] + b0);
                     const float uv = round_to<MOEQ_BF16>(acc[rt][t + 4][i] + b1);
+                    if (a.dh) {  // backward: dG, dU at the rounded G, U
+                        const size_t at = (size_t)row * a.Nout + n;
+                        float dg, du;
+                        swiglu_vjp_f(gv, uv, (float)a.dh[at], a.clamp, a.alpha, a.up_offset,
+                                     &dg, &du);
+                        a.out[at] = (__bf16)dg;
+                        a.out2[at] = (__bf16)du;
+                        continue;
+                    }
                     v = swiglu_f(gv, uv, a.clamp, a.alpha, a.up_offset);
                 } else {
                     v = acc[rt][t][i] + b0;
@@ -343,6 +354,8 @@ hipError_t run_ws(const ProjProblem &p, hipStream_t s) {
     a.clamp = p.clamp;
     a.alpha = p.alpha;
     a.up_offset = p.up_offset;
+    a.dh = static_cast<const __bf16 *>(p.in2);
+    a.out2 = static_cast<__bf16 *>(p.out2);
     const long mtiles = ((long)p.rows + kRows - 1) / kRows + p.E;
     const long blocks = 8 * ((mtiles + 7) / 8) * a.nblk;
     hipLaunchKernelGGL((awq_ws_kernel<NSETS, SD>), dim3((unsigned)blocks), dim3(kThreads), 0, s,

@@ -32,7 +32,8 @@ struct PackedOperand {
 struct ProjProblem {
     const void *in;
     void *out;
-    const void *in2;     // second input: dU (INPUT_VJP2)
+    const void *in2;     // second input: dU (INPUT_VJP2) | dh (SWIGLU backward epilogue)
+    void *out2;          // dU of the SWIGLU backward epilogue (out then holds dG)
     const int32_t *offsets;
     const int32_t *tile_offsets;  // [E+1] m-tile prefix (route), nullable
     const int32_t *tile_expert;   // expert of each m-tile (route), nullable
@@ -49,7 +50,8 @@ struct ProjProblem {
 
 enum ProjMode {
     PROJ_PLAIN = 0,      // out = in . W (+ b)
-    PROJ_SWIGLU = 1,     // out = SwiGLU(in . Wg (+ bg), in . Wu (+ bu)), AWQ
+    PROJ_SWIGLU = 1,     // out = SwiGLU(in . Wg (+ bg), in . Wu (+ bu)), AWQ; with
+                         // in2 = dh: out = dG, out2 = dU of the SwiGLU at those G, U
     PROJ_BANK_SWIGLU = 2,// MXFP4 interleaved gate/up bank + SwiGLU
     PROJ_INPUT_VJP = 3,  // out = in . W^T, AWQ (no bias)
     PROJ_INPUT_VJP2 = 4, // out = in . Wg^T + in2 . Wu^T, AWQ

@@ -195,8 +195,11 @@ def test_backward_no_tokens():
     (600, 8, 2, 512, 320, 64, "bf16", False),   # 128-row kernel, idle column waves
     (600, 8, 2, 512, 320, 32, "f16", False),    # two groups per 64 columns
     (700, 6, 3, 384, 256, 128, "f32", True),    # fp32 scales, one heavy expert
-    (40, 4, 2, 256, 192, 64, "bf16", True),     # streaming kernel, several 16-row passes
-    (50, 16, 4, 320, 128, 32, "f32", False),    # streaming kernel, g = 32, fp32 scales
+    (40, 4, 2, 256, 192, 64, "bf16", True),     # 128-row kernel, partly filled m-tiles
+    (64, 64, 2, 256, 256, 64, "bf16", True),    # streaming kernel, several 16-row passes
+    (50, 32, 4, 512, 256, 32, "f32", False),    # streaming kernel, g = 32, fp32 scales
+    (64, 64, 2, 320, 192, 64, "bf16", False),   # reductions of 64 not 256: 128-row kernel
+    (48, 64, 2, 1024, 512, 128, "bf16", True),  # streaming kernel, reduction split in two
 ])
 def test_input_vjp_kernel_paths(T, E, k, H, I, g, sdt, skew):
     """Both cubes' input VJPs and the chain across the MFMA kernels' shape cases."""
