@@ -79,7 +79,7 @@ struct WaveLds {
     uint2 U[NSETS == 2 ? kWaves / 2 : 1][4 * kRT][64];       // U tiles of the up waves
 };
 
-template <int NSETS, int SD, int SPG, int DEPTH>
+template <int NSETS, int SD, int SPG, int DEPTH, bool BWD>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 void awq_wave_kernel(WaveArgs a) {
@@ -240,6 +240,23 @@ void awq_wave_kernel(WaveArgs a) {
     const int rtn = (m1 - m0 + 15) >> 4;  // row tiles holding rows
     if constexpr (NSETS == 2) {
         const int pair = wv >> 1;  // (column group, plane)
+        // backward: the gate waves fetch their dh pairs before the U hand-off
+        // (rows past the tile reread the last row; those results are not stored)
+        uint32_t dpre[BWD ? RT : 1][4][2];
+        if constexpr (BWD) {
+            if (active && set == 0) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = min(m0 + rt * 16 + grp * 4 + i, m1 - 1);
+                        const uint32_t *dp =
+                            reinterpret_cast<const uint32_t *>(a.dh + (size_t)row * a.Nout + col0);
+                        dpre[rt][i][0] = dp[0];
+                        dpre[rt][i][1] = dp[2];
+                    }
+            }
+        }
         if (active && set == 1) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
@@ -255,7 +272,7 @@ void awq_wave_kernel(WaveArgs a) {
         }
         __syncthreads();
         if (!active || set == 1) return;
-        if (a.dh) {
+        if constexpr (BWD) {
             // backward: dG into out, dU into out2, at the rounded G, U.  The dh pair
             // at col0 holds slots (0, 2), the pair at col0 + 4 slots (1, 3).
 #pragma unroll
@@ -278,8 +295,7 @@ void awq_wave_kernel(WaveArgs a) {
                     const int row = m0 + rt * 16 + grp * 4 + i;
                     if (row >= m1) continue;
                     const size_t at = (size_t)row * a.Nout + col0;
-                    const uint32_t *dp = reinterpret_cast<const uint32_t *>(a.dh + at);
-                    const uint32_t d02 = dp[0], d13 = dp[2];
+                    const uint32_t d02 = dpre[rt][i][0], d13 = dpre[rt][i][1];
                     const float dv[4] = {__uint_as_float(d02 << 16), __uint_as_float(d13 << 16),
                                          __uint_as_float(d02 & 0xFFFF0000u),
                                          __uint_as_float(d13 & 0xFFFF0000u)};
@@ -374,12 +390,23 @@ hipError_t run_wave(const ProjProblem &p, hipStream_t s) {
     const long mtiles = ((long)p.rows + kWaveRows - 1) / kWaveRows + p.E;
     const long blocks = 8 * ((mtiles + 7) / 8) * a.nblk;
     const int spg = a.g / 32;
-    if (spg == 4)
-        hipLaunchKernelGGL((awq_wave_kernel<NSETS, SD, 4, 2>), dim3((unsigned)blocks),
-                           dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL((awq_wave_kernel<NSETS, SD, 2, 2>), dim3((unsigned)blocks),
-                           dim3(kThreads), 0, s, a);
+    // the backward epilogue is a separate instantiation: the forward kernel stays as it is
+    const bool bwd = NSETS == 2 && a.dh;
+    if (spg == 4) {
+        if (bwd)
+            hipLaunchKernelGGL((awq_wave_kernel<NSETS, SD, 4, 2, NSETS == 2>),
+                               dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((awq_wave_kernel<NSETS, SD, 4, 2, false>), dim3((unsigned)blocks),
+                               dim3(kThreads), 0, s, a);
+    } else {
+        if (bwd)
+            hipLaunchKernelGGL((awq_wave_kernel<NSETS, SD, 2, 2, NSETS == 2>),
+                               dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((awq_wave_kernel<NSETS, SD, 2, 2, false>), dim3((unsigned)blocks),
+                               dim3(kThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 
