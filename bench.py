@@ -12,6 +12,11 @@ cycle over the replicas in one graph -- and replayed.
 Prints ONE JSON line.  Default workload: the decode-shaped AWQ MoE
 (T=64, hidden 2048, intermediate 768, 128 experts, top_k 8, group 128, bf16).
 
+--path unsorted times awq_expert_forward (rows in any order with their global
+expert IDs: local sort, grouped projection, inverse permutation) on the gate cube,
+one row per assignment in token order -- the expert-parallel receive primitive.
+The call validates the IDs on the host, so it synchronises and runs eagerly.
+
 --path backward times the first-order backward path instead: one step =
 moe_combine_backward (expert rows + FP32 weights) -> awq_swiglu_input_backward
 (down VJP, recomputed gate/up with the SwiGLU VJP, both transposed cubes) ->
@@ -34,6 +39,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 METRIC = "MoE expert-FFN tokens/s at 1 GPU; % of HBM (decode) / MFMA (prefill) peak"
 METRIC_BWD = "MoE expert-FFN backward tokens/s at 1 GPU (first-order input VJPs)"
+METRIC_UNSORTED = "unsorted-row expert projection rows/s at 1 GPU (gate cube, rows in token order)"
 
 
 def parse():
@@ -45,7 +51,7 @@ def parse():
                     choices=["tiny", "decode", "prefill", "many", "mxfp4"])
     ap.add_argument("--replica-bytes", type=float, default=1.2e9,
                     help="weight bytes cycled through by consecutive steps")
-    ap.add_argument("--path", default="forward", choices=["forward", "backward"])
+    ap.add_argument("--path", default="forward", choices=["forward", "backward", "unsorted"])
     ap.add_argument("--eager", action="store_true", help="no HIP graph capture")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -274,6 +280,50 @@ def main():
                                 0.0, h)
         moeq.awq_grouped_down(route, h, w["down"], y)
         moeq.moe_combine(route, y, bufs["weights"], out)
+
+    if args.path == "unsorted":
+        if cfg.fmt != "awq":
+            print("the unsorted-row path is measured on AWQ cubes", file=sys.stderr)
+            sys.exit(2)
+        step(0)
+        xr = base["x"].repeat_interleave(k, dim=0).contiguous()   # one row per assignment
+        ids = bufs["selected"].view(-1).contiguous()               # token order, global IDs
+        yu = torch.empty(A, I, dtype=adt, device=dev)
+        wsu = torch.empty(moeq.awq_expert_workspace_bytes(A, E, H, I, adt), dtype=torch.uint8,
+                          device=dev)
+        for i in range(max(args.warmup, R)):
+            moeq.awq_expert_forward(xr, ids, replicas[i % R]["gate"], yu, wsu)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            moeq.awq_expert_forward(xr, ids, replicas[i % R]["gate"], yu, wsu)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        ab = alg_bytes(p, route.expert_offsets.cpu().numpy())
+        ub = ab["w_gateup"] // 2 + A * H * (2 if cfg.adt == "bf16" else 4) + \
+            A * I * (2 if cfg.adt == "bf16" else 4)
+        uf = 2 * A * H * I
+        ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if uf / ub > ridge:
+            bound, peak, unit, achieved = "mfma", BF16_PEAK_TFLOPS, "TFLOP/s", uf / (ms * 1e-3) / 1e12
+        else:
+            bound, peak, unit, achieved = "hbm", HBM_PEAK_GBS, "GB/s", ub / (ms * 1e-3) / 1e9
+        res = {
+            "metric": METRIC_UNSORTED, "value": round(A / (ms * 1e-3), 1), "unit": "rows/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16" if cfg.adt == "bf16" else "f32", "data": "synthetic",
+            "config": {"workload": workload_name(cfg), "rows": A, "touched_experts": ab["touched"],
+                       "weight_replicas": R, "graph": False, "path": "unsorted"},
+            "roofline": {"kernel": "awq_expert_forward (host ID check + sort + gather + "
+                                   "grouped projection + restore), host clock",
+                         "bound": bound, "achieved": round(achieved, 1), "peak": peak,
+                         "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                         "kernel_ms": round(ms, 5), "alg_bytes_per_launch": ub,
+                         "alg_flops_per_launch": uf},
+        }
+        print(json.dumps(res), flush=True)
+        return
 
     backward = args.path == "backward"
     if backward:

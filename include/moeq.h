@@ -17,6 +17,9 @@
  *   moe_dispatch_backward          COPY VJP back to the source tokens
  *   moe_dispatch_weights_backward  fixed-selection router-logit VJP
  *
+ * Rows in any order (the expert-parallel receive side, and single projections):
+ *   awq_expert_forward, awq_expert_input_backward, frozen_awq_forward
+ *
  * Sources (the pages the operations are defined on):
  *   ruda-tensor 0.21.38 src/moe_exchange.rs    -- MoeDispatched, MoeDispatchOps
  *   ruda-tensor 0.21.34 src/packed_experts.rs  -- AwqExpertOptions,
@@ -295,6 +298,59 @@ moeq_status awq_swiglu_input_backward(const moeq_route *route, const void *value
                                       const moeq_experts *up, const moeq_experts *down,
                                       moeq_swiglu fn, const void *grad, void *grad_values,
                                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * awq_expert_forward -- packed_experts.rs FrozenPackedExpertOps::
+ * packed_expert_forward: rows in any order, each with its global expert ID;
+ * only the experts that occur are evaluated and the output keeps the incoming
+ * row order:
+ *   y[t, :] = round_act( x[t, :] . W_{id[t]} (+ b_{id[t]}) )
+ * It is also the receive side of moe_exchange.rs MoeReceivedOps::
+ * moe_received_forward: a local sort by global ID, the grouped expert kernels,
+ * and the inverse permutation.
+ *   x [rows, K] act, global_ids [rows] u32 (device), y [rows, N] act.
+ *   w: an AWQ cube or a non-interleaved MXFP4 bank; IDs must lie in
+ *      [expert_start, expert_start + experts), else ERANGE.  Experts that no
+ *      row names are never read (empty owners are allowed).
+ * The IDs are validated on the host: the call copies them and synchronises
+ * `stream` before it enqueues the sort, the gather, the projection and the
+ * restore.  workspace: device, 256-byte aligned, caller-owned,
+ * >= awq_expert_workspace_bytes(rows, experts, K, N, act).  Implemented for
+ * experts <= 2048 (else EUNSUPPORTED).  rows = 0: no-op.
+ */
+size_t awq_expert_workspace_bytes(int32_t rows, int32_t experts, int32_t in_features,
+                                  int32_t out_features, moeq_dtype act);
+
+moeq_status awq_expert_forward(const void *x, moeq_dtype act, int32_t rows,
+                               const uint32_t *global_ids, const moeq_experts *w, void *y,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * awq_expert_input_backward -- packed_experts.rs FrozenPackedExpertOps::
+ * packed_expert_input_backward for awq_expert_forward: the transpose of the same
+ * rounded coefficients, rows in the incoming order:
+ *   grad_in[t, :] = round_gdt( grad[t, :] . W_{id[t]}^T )
+ *   grad [rows, N] gdt, grad_in [rows, K] gdt (F32 or BF16); AWQ only.
+ * Same IDs, validation, synchronisation and workspace as awq_expert_forward.
+ */
+moeq_status awq_expert_input_backward(const void *grad, moeq_dtype gdt, int32_t rows,
+                                      const uint32_t *global_ids, const moeq_experts *w,
+                                      void *grad_in, void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
+/*
+ * frozen_awq_forward -- frozen_awq.rs FrozenAwqOps::frozen_awq_forward: one packed
+ * projection over all rows, y = round_act(x . W (+ b)).  w holds one expert
+ * (experts == 1, else ERANGE): AWQ words [1, K, N/8] or a non-interleaved MXFP4
+ * bank.  x [rows, K] act, y [rows, N] act.  workspace: device, 256-byte aligned,
+ * >= frozen_awq_workspace_bytes(rows) (the kernels' row map).  Its input VJP is
+ * awq_input_backward with route NULL.
+ */
+size_t frozen_awq_workspace_bytes(int32_t rows);
+
+moeq_status frozen_awq_forward(const void *x, moeq_dtype act, int32_t rows,
+                               const moeq_experts *w, void *y, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 /* Static text for a status code. */
 const char *moeq_status_string(moeq_status status);

@@ -149,6 +149,36 @@ moeq_status check_experts(const moeq_experts *w, const char *name, int route_E, 
     return MOEQ_OK;
 }
 
+// Workspace of the unsorted-row calls: a route for (rows, experts, top_k 1), the local
+// expert IDs, the sorted rows' expert IDs, and the sorted input and output rows.
+struct UnsortedLayout {
+    size_t route, local, rex, xs, ys, total;
+};
+
+bool unsorted_layout(int32_t rows, int32_t experts, int32_t K, int32_t N, int act,
+                     UnsortedLayout *L) {
+    Layout r;
+    if (rows < 0 || K < 1 || N < 1 || !valid_dtype(act) || !route_layout(rows, experts, 1, &r))
+        return false;
+    size_t row_bytes;
+    if (!mul_ok((size_t)(K > N ? K : N), dtype_bytes(act), &row_bytes)) return false;
+    size_t tile;
+    if (!mul_ok((size_t)(rows ? rows : 1), row_bytes, &tile)) return false;
+    size_t o = 0;
+    L->route = o;
+    o += align256(r.total);
+    L->local = o;
+    o += align256(sizeof(uint32_t) * (size_t)(rows ? rows : 1));
+    L->rex = o;
+    o += align256(sizeof(uint32_t) * (size_t)(rows ? rows : 1));
+    L->xs = o;
+    o += align256(tile);
+    L->ys = o;
+    o += align256(tile);
+    L->total = o;
+    return true;
+}
+
 PackedOperand operand_of(const moeq_experts *w) {
     PackedOperand o;
     o.format = w->format;
@@ -588,6 +618,204 @@ moeq_status awq_swiglu_input_backward(const moeq_route *route, const void *value
     q.mode = PROJ_INPUT_VJP2;
     return device_status(vjp_fits(q) ? launch_vjp(q, s) : launch_proj_generic(q, s),
                          "gate/up input VJP");
+}
+
+// ---------------------------------------------------------------- unsorted rows
+
+size_t awq_expert_workspace_bytes(int32_t rows, int32_t experts, int32_t K, int32_t N,
+                                  moeq_dtype act) {
+    UnsortedLayout L;
+    return unsorted_layout(rows, experts, K, N, act, &L) ? L.total : 0;
+}
+
+namespace {
+
+// Shared by awq_expert_forward and awq_expert_input_backward: validation of the
+// IDs on the host, then the local stable sort by expert (route of top_k 1) and the
+// gather of the incoming rows into expert order.
+moeq_status unsorted_prepare(const void *in, int act, int32_t rows, int32_t in_cols,
+                             const uint32_t *global_ids, const moeq_experts *w, int32_t K,
+                             int32_t N, void *workspace, size_t workspace_bytes, hipStream_t s,
+                             moeq_route *route, UnsortedLayout *L) {
+    moeq_status st;
+    if (!unsorted_layout(rows, w->experts, K, N, act, L))
+        return fail(MOEQ_ESHAPE, "invalid sizes or size overflow");
+    if (!workspace) return fail(MOEQ_EINVAL, "workspace is NULL");
+    if ((uintptr_t)workspace % 256 != 0)
+        return fail(MOEQ_EWORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < L->total)
+        return fail(MOEQ_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                    L->total);
+    if (!in || !global_ids) return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    // the pages return an error for an ID outside the resident range: check on the host
+    std::vector<uint32_t> ids((size_t)rows);
+    if ((st = device_status(hipMemcpyAsync(ids.data(), global_ids, sizeof(uint32_t) * ids.size(),
+                                           hipMemcpyDeviceToHost, s),
+                            "ID copy")) != MOEQ_OK)
+        return st;
+    if ((st = device_status(hipStreamSynchronize(s), "stream sync")) != MOEQ_OK) return st;
+    const uint64_t lo = (uint64_t)w->expert_start, hi = lo + (uint64_t)w->experts;
+    for (int32_t t = 0; t < rows; ++t)
+        if (ids[t] < lo || ids[t] >= hi)
+            return fail(MOEQ_ERANGE, "global_ids[%d] = %u outside the resident experts [%llu, %llu)",
+                        t, ids[t], (unsigned long long)lo, (unsigned long long)hi);
+    char *base = static_cast<char *>(workspace);
+    if ((st = moeq_route_bind(route, base + L->route, workspace_bytes - L->route, rows,
+                              w->experts, 1)) != MOEQ_OK)
+        return st;
+    uint32_t *local = reinterpret_cast<uint32_t *>(base + L->local);
+    uint32_t *rex = reinterpret_cast<uint32_t *>(base + L->rex);
+    if ((st = device_status(launch_local_ids(global_ids, rows, w->expert_start, local, s),
+                            "local IDs")) != MOEQ_OK)
+        return st;
+    if ((st = device_status(launch_dispatch_index(local, rows, w->experts, 1, route, rex, s),
+                            "local sort")) != MOEQ_OK)
+        return st;
+    return device_status(launch_copy_rows(in, (size_t)in_cols * dtype_bytes(act), rows,
+                                          route->row_src, base + L->xs, s),
+                         "row gather");
+}
+
+}  // namespace
+
+moeq_status awq_expert_forward(const void *x, moeq_dtype act, int32_t rows,
+                               const uint32_t *global_ids, const moeq_experts *w, void *y,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    moeq_status st;
+    if (!valid_dtype(act)) return fail(MOEQ_EDTYPE, "unknown activation dtype %d", (int)act);
+    if (rows < 0) return fail(MOEQ_EINVAL, "rows must be >= 0");
+    if ((st = check_experts(w, "weights", -1, -1, -1, false)) != MOEQ_OK) return st;
+    if (w->experts > kMaxExperts)
+        return fail(MOEQ_EUNSUPPORTED, "the local sort implements up to %d experts", kMaxExperts);
+    if (act == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 activations are not implemented");
+    const int K = w->in_features, N = w->out_features;
+    if (rows == 0) return MOEQ_OK;
+    if (!y) return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    moeq_route route;
+    UnsortedLayout L;
+    if ((st = unsorted_prepare(x, act, rows, K, global_ids, w, K, N, workspace, workspace_bytes,
+                               s, &route, &L)) != MOEQ_OK)
+        return st;
+    char *base = static_cast<char *>(workspace);
+    ProjProblem p{};
+    p.in = base + L.xs;
+    p.out = base + L.ys;
+    p.offsets = route.expert_offsets;
+    p.tile_offsets = route.tile_offsets;
+    p.tile_expert = route.tile_expert;
+    p.rows = rows;
+    p.E = w->experts;
+    p.act = act;
+    p.Kred = K;
+    p.Nout = N;
+    p.w0 = p.w1 = operand_of(w);
+    p.mode = PROJ_PLAIN;
+    bool handled = false;
+    hipError_t err = launch_fast_plain(p, s, &handled);
+    if (!handled) err = launch_proj_generic(p, s);
+    if ((st = device_status(err, "projection")) != MOEQ_OK) return st;
+    // inverse permutation: incoming row t is sorted row slot_pos[t]
+    return device_status(launch_copy_rows(base + L.ys, (size_t)N * dtype_bytes(act), rows,
+                                          route.slot_pos, y, s),
+                         "row restore");
+}
+
+moeq_status awq_expert_input_backward(const void *grad, moeq_dtype gdt, int32_t rows,
+                                      const uint32_t *global_ids, const moeq_experts *w,
+                                      void *grad_in, void *workspace, size_t workspace_bytes,
+                                      void *stream) {
+    moeq_status st;
+    if (!valid_dtype(gdt)) return fail(MOEQ_EDTYPE, "unknown gradient dtype %d", (int)gdt);
+    if (rows < 0) return fail(MOEQ_EINVAL, "rows must be >= 0");
+    if ((st = check_experts(w, "weights", -1, -1, -1, false)) != MOEQ_OK) return st;
+    if (w->format != MOEQ_FMT_AWQ)
+        return fail(MOEQ_EUNSUPPORTED, "input VJP is implemented for AWQ cubes");
+    if (w->experts > kMaxExperts)
+        return fail(MOEQ_EUNSUPPORTED, "the local sort implements up to %d experts", kMaxExperts);
+    if (gdt == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 gradients are not implemented");
+    const int K = w->in_features, N = w->out_features;
+    if (rows == 0) return MOEQ_OK;
+    if (!grad_in) return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    moeq_route route;
+    UnsortedLayout L;
+    if ((st = unsorted_prepare(grad, gdt, rows, N, global_ids, w, K, N, workspace,
+                               workspace_bytes, s, &route, &L)) != MOEQ_OK)
+        return st;
+    char *base = static_cast<char *>(workspace);
+    ProjProblem p{};
+    p.in = base + L.xs;
+    p.out = base + L.ys;
+    p.offsets = route.expert_offsets;
+    p.tile_offsets = route.tile_offsets;
+    p.tile_expert = route.tile_expert;
+    p.rows = rows;
+    p.E = w->experts;
+    p.act = gdt;
+    p.Kred = N;
+    p.Nout = K;
+    p.w0 = p.w1 = operand_of(w);
+    p.mode = PROJ_INPUT_VJP;
+    if ((st = device_status(vjp_fits(p) ? launch_vjp(p, s) : launch_proj_generic(p, s),
+                            "input VJP")) != MOEQ_OK)
+        return st;
+    return device_status(launch_copy_rows(base + L.ys, (size_t)K * dtype_bytes(gdt), rows,
+                                          route.slot_pos, grad_in, s),
+                         "row restore");
+}
+
+size_t frozen_awq_workspace_bytes(int32_t rows) {
+    if (rows < 0) return 0;
+    // offsets [2], m-tile prefix [2], expert of each m-tile
+    return align256(2 * sizeof(int32_t)) * 2 +
+           align256(sizeof(int32_t) * ((size_t)(rows + kTileRows - 1) / kTileRows + 1));
+}
+
+moeq_status frozen_awq_forward(const void *x, moeq_dtype act, int32_t rows,
+                               const moeq_experts *w, void *y, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    moeq_status st;
+    if (!valid_dtype(act)) return fail(MOEQ_EDTYPE, "unknown activation dtype %d", (int)act);
+    if (rows < 0) return fail(MOEQ_EINVAL, "rows must be >= 0");
+    if ((st = check_experts(w, "weights", -1, -1, -1, false)) != MOEQ_OK) return st;
+    if (w->experts != 1)
+        return fail(MOEQ_ERANGE, "a single frozen projection holds one expert, has %d",
+                    w->experts);
+    if (act == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 activations are not implemented");
+    if (rows == 0) return MOEQ_OK;
+    if (!x || !y) return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    const size_t need = frozen_awq_workspace_bytes(rows);
+    if (!workspace) return fail(MOEQ_EINVAL, "workspace is NULL");
+    if ((uintptr_t)workspace % 256 != 0)
+        return fail(MOEQ_EWORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(MOEQ_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    char *base = static_cast<char *>(workspace);
+    int32_t *offsets = reinterpret_cast<int32_t *>(base);
+    int32_t *tile_offsets = reinterpret_cast<int32_t *>(base + align256(2 * sizeof(int32_t)));
+    int32_t *tile_expert = reinterpret_cast<int32_t *>(base + 2 * align256(2 * sizeof(int32_t)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = device_status(launch_single_tiles(rows, offsets, tile_offsets, tile_expert, s),
+                            "row map")) != MOEQ_OK)
+        return st;
+    ProjProblem p{};
+    p.in = x;
+    p.out = y;
+    p.offsets = offsets;
+    p.tile_offsets = tile_offsets;
+    p.tile_expert = tile_expert;
+    p.rows = rows;
+    p.E = 1;
+    p.act = act;
+    p.Kred = w->in_features;
+    p.Nout = w->out_features;
+    p.w0 = p.w1 = operand_of(w);
+    p.mode = PROJ_PLAIN;
+    bool handled = false;
+    hipError_t err = launch_fast_plain(p, s, &handled);
+    if (!handled) err = launch_proj_generic(p, s);
+    return device_status(err, "frozen projection");
 }
 
 }  // extern "C"

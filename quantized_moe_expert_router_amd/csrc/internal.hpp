@@ -69,6 +69,10 @@ hipError_t launch_dispatch_index(const uint32_t *selected, int T, int E, int k,
                                  hipStream_t s);
 hipError_t launch_copy_rows(const void *x, size_t row_bytes, int A, const int32_t *row_src,
                             void *values, hipStream_t s);
+hipError_t launch_local_ids(const uint32_t *gid, int rows, int start, uint32_t *local,
+                            hipStream_t s);
+hipError_t launch_single_tiles(int rows, int32_t *offsets, int32_t *tile_offsets,
+                               int32_t *tile_expert, hipStream_t s);
 hipError_t launch_combine(const void *y, int act, const float *weights,
                           const int32_t *slot_pos, int T, int k, int K, void *out,
                           hipStream_t s);

@@ -460,6 +460,46 @@ hipError_t launch_dispatch_index(const uint32_t *selected, int T, int E, int k,
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ unsorted rows
+// Local expert index of each incoming row (IDs validated on the host).
+__global__ __launch_bounds__(256) void local_ids_kernel(const uint32_t *__restrict__ gid, int rows,
+                                                        uint32_t start,
+                                                        uint32_t *__restrict__ local) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < rows) local[t] = gid[t] - start;
+}
+
+hipError_t launch_local_ids(const uint32_t *gid, int rows, int start, uint32_t *local,
+                            hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(local_ids_kernel, dim3((rows + 255) / 256), dim3(256), 0, s, gid, rows,
+                       (uint32_t)start, local);
+    return hipGetLastError();
+}
+
+// Row map of a single cube over all rows: offsets {0, rows}, 128-row m-tiles.
+__global__ __launch_bounds__(256) void single_tiles_kernel(int rows, int32_t *__restrict__ offsets,
+                                                           int32_t *__restrict__ tile_offsets,
+                                                           int32_t *__restrict__ tile_expert) {
+    const int nt = (rows + kTileRows - 1) / kTileRows;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i == 0) {
+        offsets[0] = 0;
+        offsets[1] = rows;
+        tile_offsets[0] = 0;
+        tile_offsets[1] = nt;
+    }
+    if (i < nt) tile_expert[i] = 0;
+}
+
+hipError_t launch_single_tiles(int rows, int32_t *offsets, int32_t *tile_offsets,
+                               int32_t *tile_expert, hipStream_t s) {
+    const int nt = (rows + kTileRows - 1) / kTileRows;
+    hipLaunchKernelGGL(single_tiles_kernel, dim3((nt + 255) / 256 + 1), dim3(256), 0, s, rows,
+                       offsets, tile_offsets, tile_expert);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ row copy
 template <typename V>
 __global__ __launch_bounds__(256) void copy_rows_kernel(const V *__restrict__ x,

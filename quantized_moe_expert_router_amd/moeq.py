@@ -29,7 +29,9 @@ EXPORTS = ("moeq_route_workspace_bytes", "moeq_route_bind", "moe_dispatch",
            "moe_dispatch_counts", "awq_grouped_swiglu", "awq_grouped_down", "moe_combine",
            "awq_input_backward", "moe_combine_backward", "moe_dispatch_backward",
            "moe_dispatch_weights_backward", "awq_swiglu_input_backward_workspace_bytes",
-           "awq_swiglu_input_backward", "moeq_status_string", "moeq_last_error")
+           "awq_swiglu_input_backward", "awq_expert_workspace_bytes", "awq_expert_forward",
+           "awq_expert_input_backward", "frozen_awq_workspace_bytes", "frozen_awq_forward",
+           "moeq_status_string", "moeq_last_error")
 
 
 class MoeqError(RuntimeError):
@@ -105,6 +107,19 @@ def lib():
     L.awq_swiglu_input_backward.argtypes = [C.POINTER(Route), vp, C.c_int, C.POINTER(Experts),
                                             C.POINTER(Experts), C.POINTER(Experts), SwiGLU, vp,
                                             vp, vp, C.c_size_t, vp]
+    L.awq_expert_workspace_bytes.restype = C.c_size_t
+    L.awq_expert_workspace_bytes.argtypes = [i32, i32, i32, i32, C.c_int]
+    L.awq_expert_forward.restype = C.c_int
+    L.awq_expert_forward.argtypes = [vp, C.c_int, i32, vp, C.POINTER(Experts), vp, vp,
+                                     C.c_size_t, vp]
+    L.awq_expert_input_backward.restype = C.c_int
+    L.awq_expert_input_backward.argtypes = [vp, C.c_int, i32, vp, C.POINTER(Experts), vp, vp,
+                                            C.c_size_t, vp]
+    L.frozen_awq_workspace_bytes.restype = C.c_size_t
+    L.frozen_awq_workspace_bytes.argtypes = [i32]
+    L.frozen_awq_forward.restype = C.c_int
+    L.frozen_awq_forward.argtypes = [vp, C.c_int, i32, C.POINTER(Experts), vp, vp, C.c_size_t,
+                                     vp]
     L.moeq_status_string.restype = C.c_char_p
     L.moeq_status_string.argtypes = [C.c_int]
     L.moeq_last_error.restype = C.c_char_p
@@ -357,6 +372,67 @@ def awq_swiglu_input_backward(route: RouteState, values: torch.Tensor, gate: Awq
                                            _ptr(grad_values), _ptr(workspace),
                                            workspace.numel(), _stream(values.device)))
     return grad_values
+
+
+# ------------------------------------------------------------------ rows in any order
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def awq_expert_workspace_bytes(rows: int, experts: int, in_features: int, out_features: int,
+                               dtype: torch.dtype) -> int:
+    return int(lib().awq_expert_workspace_bytes(rows, experts, in_features, out_features,
+                                                _TORCH_DT.get(dtype, 99)))
+
+
+def awq_expert_forward(x: torch.Tensor, global_ids: torch.Tensor, w,
+                       y: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rows in any order, each with its global expert ID; output in the incoming
+    order (packed_experts.rs packed_expert_forward).  Synchronises (ID check)."""
+    wc = w.c()
+    rows = x.shape[0]
+    if y is None:
+        y = torch.empty(rows, wc.out_features, dtype=x.dtype, device=x.device)
+    nbytes = lib().awq_expert_workspace_bytes(rows, wc.experts, wc.in_features,
+                                              wc.out_features, _dt(x))
+    workspace = _workspace(nbytes, x.device, workspace)
+    _check(lib().awq_expert_forward(_ptr(x), _dt(x), rows, _ptr(global_ids), C.byref(wc),
+                                    _ptr(y), _ptr(workspace), workspace.numel(),
+                                    _stream(x.device)))
+    return y
+
+
+def awq_expert_input_backward(grad: torch.Tensor, global_ids: torch.Tensor, w: AwqExperts,
+                              grad_in: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Input VJP of awq_expert_forward, rows in the incoming order."""
+    wc = w.c()
+    rows = grad.shape[0]
+    if grad_in is None:
+        grad_in = torch.empty(rows, wc.in_features, dtype=grad.dtype, device=grad.device)
+    nbytes = lib().awq_expert_workspace_bytes(rows, wc.experts, wc.in_features,
+                                              wc.out_features, _dt(grad))
+    workspace = _workspace(nbytes, grad.device, workspace)
+    _check(lib().awq_expert_input_backward(_ptr(grad), _dt(grad), rows, _ptr(global_ids),
+                                           C.byref(wc), _ptr(grad_in), _ptr(workspace),
+                                           workspace.numel(), _stream(grad.device)))
+    return grad_in
+
+
+def frozen_awq_forward(x: torch.Tensor, w, y: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One packed projection (a one-expert cube) over all rows (frozen_awq.rs)."""
+    wc = w.c()
+    rows = x.shape[0]
+    if y is None:
+        y = torch.empty(rows, wc.out_features, dtype=x.dtype, device=x.device)
+    workspace = _workspace(lib().frozen_awq_workspace_bytes(rows), x.device, workspace)
+    _check(lib().frozen_awq_forward(_ptr(x), _dt(x), rows, C.byref(wc), _ptr(y),
+                                    _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return y
 
 
 def moe_ffn(x, logits, expert_bias, top_k, gate, up, down, clamp=0.0, alpha=1.0, up_offset=0.0):

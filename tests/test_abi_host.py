@@ -256,3 +256,61 @@ def test_backward_path_validation(L):
     assert sib(r, act=moeq.F16) == moeq.EUNSUPPORTED
     assert sib(r, fn=(-2.0, 1.0, 0.0)) == moeq.EINVAL
     assert sib(r, down=awq(E=4, K=32, N=64)) == moeq.ERANGE
+
+
+def test_unsorted_and_single_projection_validation(L):
+    """packed_experts.rs packed_expert_forward / packed_expert_input_backward and
+    frozen_awq.rs frozen_awq_forward: every case fails validation before any device
+    work, or is a no-op (rows = 0)."""
+    P = C.c_void_p(FAKE)
+    ws = L.awq_expert_workspace_bytes
+    assert ws(100, 8, 64, 32, moeq.BF16) > 0 and ws(100, 8, 64, 32, moeq.BF16) % 256 == 0
+    assert ws(0, 8, 64, 32, moeq.BF16) > 0
+    assert ws(-1, 8, 64, 32, moeq.BF16) == 0 and ws(4, 0, 64, 32, moeq.BF16) == 0
+    assert ws(4, 8, 0, 32, moeq.BF16) == 0 and ws(4, 8, 64, 32, 5) == 0
+    need = ws(100, 8, 64, 32, moeq.BF16)
+
+    def fwd(rows=100, w=None, act=moeq.BF16, x=FAKE, ids=FAKE, y=FAKE, wsp=FAKE, nbytes=need):
+        w = w or awq(E=8, K=64, N=32)
+        v = lambda a: C.c_void_p(a) if a else None
+        return L.awq_expert_forward(v(x), act, rows, v(ids), C.byref(w), v(y), v(wsp), nbytes,
+                                    None)
+    assert fwd(rows=0) == moeq.OK
+    assert fwd(rows=-1) == moeq.EINVAL
+    assert fwd(act=4) == moeq.EDTYPE
+    assert fwd(act=moeq.F16) == moeq.EUNSUPPORTED
+    assert fwd(w=awq(E=8, K=64, N=36)) == moeq.ESHAPE
+    assert fwd(w=awq(E=4096, K=64, N=32)) == moeq.EUNSUPPORTED
+    assert fwd(y=0) == moeq.EINVAL
+    assert fwd(wsp=0) == moeq.EINVAL
+    assert fwd(wsp=FAKE + 64) == moeq.EWORKSPACE
+    assert fwd(nbytes=need - 1) == moeq.EWORKSPACE
+    assert fwd(x=0) == moeq.EINVAL
+    assert fwd(ids=0) == moeq.EINVAL
+    assert fwd(w=bank(E=8, K=64, R=32, inter=1)) == moeq.ESHAPE   # a plain role takes a plain bank
+
+    def bwd(rows=100, w=None, gdt=moeq.BF16, wsp=FAKE, nbytes=need):
+        w = w or awq(E=8, K=64, N=32)
+        return L.awq_expert_input_backward(P, gdt, rows, P, C.byref(w), P,
+                                           C.c_void_p(wsp) if wsp else None, nbytes, None)
+    assert bwd(rows=0) == moeq.OK
+    assert bwd(gdt=moeq.F16) == moeq.EUNSUPPORTED
+    assert bwd(w=bank(E=8, K=64, R=32, inter=0)) == moeq.EUNSUPPORTED
+    assert bwd(wsp=0) == moeq.EINVAL
+    assert bwd(nbytes=16) == moeq.EWORKSPACE
+
+    fw = L.frozen_awq_workspace_bytes
+    assert fw(0) > 0 and fw(1000) >= fw(10) and fw(-1) == 0
+    need1 = fw(300)
+
+    def single(rows=300, w=None, act=moeq.BF16, wsp=FAKE, nbytes=need1, x=FAKE):
+        w = w or awq(E=1, K=64, N=32)
+        return L.frozen_awq_forward(C.c_void_p(x) if x else None, act, rows, C.byref(w), P,
+                                    C.c_void_p(wsp) if wsp else None, nbytes, None)
+    assert single(rows=0) == moeq.OK
+    assert single(w=awq(E=2, K=64, N=32)) == moeq.ERANGE
+    assert single(act=moeq.F16) == moeq.EUNSUPPORTED
+    assert single(x=0) == moeq.EINVAL
+    assert single(wsp=0) == moeq.EINVAL
+    assert single(nbytes=need1 - 1) == moeq.EWORKSPACE
+    assert single(wsp=FAKE + 8) == moeq.EWORKSPACE
