@@ -142,11 +142,16 @@ typedef struct moeq_experts {
 
 /* SwiGLU parameters: h = g' * sigmoid(alpha * g') * (u' + up_offset) with
  * g', u' clamped to [-clamp, clamp] when clamp > 0.  Plain SwiGLU is
- * {0, 1, 0}; the clamped routed variant of native.rs's engine is {7, 1, 0}. */
+ * {0, 1, 0, 0}; the clamped routed variant of native.rs's engine is
+ * {7, 1, 0, 0}.  gate_one_sided = 1 clamps the gate from above only,
+ * g' = min(g, clamp) (u' unchanged): with {7, 1.702, 1, 1} it is the form some
+ * MXFP4 models use.  A clamped value passes the derivative on its closed
+ * interval (the backward path) and blocks it outside. */
 typedef struct moeq_swiglu {
     float clamp;
     float alpha;
     float up_offset;
+    int32_t gate_one_sided;  /* 0 or 1 */
 } moeq_swiglu;
 
 /*

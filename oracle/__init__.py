@@ -52,7 +52,8 @@ def _load():
     lib.orc_awq_dequant.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, vp]
     lib.orc_awq_project.argtypes = [i32, i32, i32, vp, i32, vp, i32, i32, vp, vp, vp, i32,
                                     vp, vp, vp]
-    lib.orc_swiglu.argtypes = [C.c_size_t, vp, vp, i32, C.c_double, C.c_double, C.c_double, vp]
+    lib.orc_swiglu.argtypes = [C.c_size_t, vp, vp, i32, C.c_double, C.c_double, C.c_double,
+                               i32, vp]
     lib.orc_combine.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp]
     lib.orc_copy_vjp.argtypes = [i32, i32, i32, vp, vp, vp]
     lib.orc_awq_input_backward.argtypes = [i32, i32, i32, vp, i32, vp, i32, i32, vp, vp, vp,
@@ -61,10 +62,11 @@ def _load():
     lib.orc_dispatch_weights_backward.argtypes = [i32, i32, i32, vp, vp, vp, vp]
     lib.orc_combine_backward.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp, vp, vp]
     lib.orc_swiglu_backward.argtypes = [C.c_size_t, vp, vp, vp, i32, C.c_double, C.c_double,
-                                        C.c_double, vp, vp]
+                                        C.c_double, i32, vp, vp]
     lib.orc_awq_swiglu_input_backward.argtypes = [i32, i32, i32, vp, i32, vp, i32, i32,
                                                   vp, vp, vp, vp, vp, vp, i32, vp, vp,
-                                                  C.c_double, C.c_double, C.c_double, vp, vp]
+                                                  C.c_double, C.c_double, C.c_double, i32,
+                                                  vp, vp]
     lib.orc_e2m1_value.restype = C.c_double
     lib.orc_e2m1_value.argtypes = [i32]
     lib.orc_e8m0_value.restype = C.c_double
@@ -198,12 +200,12 @@ def awq_project(x, adt, row_experts, qweight, qzeros, scales, sdt, g, bias=None,
     return (out, exact) if want_exact else out
 
 
-def swiglu(G, U, adt, clamp=0.0, alpha=1.0, up_offset=0.0):
+def swiglu(G, U, adt, clamp=0.0, alpha=1.0, up_offset=0.0, gate_one_sided=False):
     G = _store(G, adt)
     U = _store(U, adt)
     h = np.zeros_like(G)
     _load().orc_swiglu(G.size, _p(G), _p(U), DT[adt], float(clamp), float(alpha),
-                       float(up_offset), _p(h))
+                       float(up_offset), int(bool(gate_one_sided)), _p(h))
     return h
 
 
@@ -283,7 +285,7 @@ def combine_backward(y, adt, weights, slot_pos, dout, want_dy=True, want_dweight
     return dy, dw
 
 
-def swiglu_backward(G, U, dh, adt, clamp=0.0, alpha=1.0, up_offset=0.0):
+def swiglu_backward(G, U, dh, adt, clamp=0.0, alpha=1.0, up_offset=0.0, gate_one_sided=False):
     """SwiGLU VJP at the forward's storage-rounded G, U: (dG, dU) in adt."""
     G = _store(G, adt)
     U = _store(U, adt)
@@ -291,12 +293,13 @@ def swiglu_backward(G, U, dh, adt, clamp=0.0, alpha=1.0, up_offset=0.0):
     dG = np.zeros_like(G)
     dU = np.zeros_like(G)
     _load().orc_swiglu_backward(G.size, _p(G), _p(U), _p(dh), DT[adt], float(clamp),
-                                float(alpha), float(up_offset), _p(dG), _p(dU))
+                                float(alpha), float(up_offset), int(bool(gate_one_sided)),
+                                _p(dG), _p(dU))
     return dG, dU
 
 
 def awq_swiglu_input_backward(values, adt, row_experts, gate, up, sdt, g, dh, clamp=0.0,
-                              alpha=1.0, up_offset=0.0):
+                              alpha=1.0, up_offset=0.0, gate_one_sided=False):
     """Input VJP of the gate/up + SwiGLU part: dvalues [A, K] adt.
     gate / up: (qweight, qzeros, scales, bias or None) of equal shape."""
     values = _store(values, adt)
@@ -317,7 +320,8 @@ def awq_swiglu_input_backward(values, adt, row_experts, gate, up, sdt, g, dh, cl
     _load().orc_awq_swiglu_input_backward(A, K, I, _p(values), DT[adt], _p(rex), E, g,
                                           _p(gqw), _p(gqz), _p(gs), _p(uqw), _p(uqz), _p(us),
                                           DT[sdt], _p(gb), _p(ub), float(clamp), float(alpha),
-                                          float(up_offset), _p(dh), _p(out))
+                                          float(up_offset), int(bool(gate_one_sided)), _p(dh),
+                                          _p(out))
     return out
 
 
@@ -360,7 +364,7 @@ class _MoeArgs(C.Structure):
         ("gu_blocks", C.c_void_p), ("gu_scales", C.c_void_p), ("dn_blocks", C.c_void_p),
         ("dn_scales", C.c_void_p), ("gu_bias", C.c_void_p), ("dn_bias", C.c_void_p),
         ("clamp", C.c_double), ("alpha", C.c_double), ("up_offset", C.c_double),
-        ("out", C.c_void_p),
+        ("gate_one_sided", C.c_int), ("out", C.c_void_p),
         ("selected", C.c_void_p), ("weights", C.c_void_p), ("offsets", C.c_void_p),
         ("row_src", C.c_void_p), ("slot_pos", C.c_void_p), ("row_experts", C.c_void_p),
         ("values", C.c_void_p), ("h", C.c_void_p), ("y", C.c_void_p),
@@ -412,6 +416,7 @@ def moe_forward(p: dict, keep_intermediates: bool = True) -> dict:
     args.clamp = float(p.get("clamp", 0.0))
     args.alpha = float(p.get("alpha", 1.0))
     args.up_offset = float(p.get("up_offset", 0.0))
+    args.gate_one_sided = int(bool(p.get("gate_one_sided", False)))
     st = NP_STORAGE[adt]
     res = {"out": np.zeros((T, H), st)}
     args.out = res["out"].ctypes.data_as(C.c_void_p).value

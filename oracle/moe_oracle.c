@@ -24,7 +24,7 @@
  *                                   (tests/golden/awq_words.txt); worked
  *                                   rounding values; numpy f16 casts
  *   orc_awq_project                 numpy float64 matmul, exact-arithmetic cases
- *   orc_swiglu                      scipy expit, clamp bound
+ *   orc_swiglu                      scipy expit, clamp bound, one-sided gate clamp
  *   orc_combine                     order-sensitive fp32 case, k*x identity
  *   orc_copy_vjp                    adjoint identity with the COPY dispatch
  *   orc_awq_input_backward          adjoint identity, numpy matmul
@@ -394,16 +394,24 @@ void orc_awq_project(int A, int K, int N, const void *in, int adt,
 /* packed_experts.rs FrozenPackedExpertOps::packed_swiglu_forward: gate/up/down
  * chain with storage-rounded SwiGLU.  h = g' * sigmoid(alpha*g') * (u' + off),
  * g' and u' clamped to [-clamp, clamp] when clamp > 0 (the clamped variant of
- * libmir-metal's clamped_routed engine), in double, rounded once to adt. */
-void orc_swiglu(size_t n, const void *G, const void *U, int adt, double clamp,
-                double alpha, double up_offset, void *h)
+ * libmir-metal's clamped_routed engine), in double, rounded once to adt.
+ * gate_one_sided != 0 is the variant some MXFP4 models use: the gate is clamped
+ * from above only, g' = min(g, clamp), u' as before. */
+static double gate_lower(double clamp, int gate_one_sided)
 {
+    return gate_one_sided ? -INFINITY : -clamp;
+}
+
+void orc_swiglu(size_t n, const void *G, const void *U, int adt, double clamp,
+                double alpha, double up_offset, int gate_one_sided, void *h)
+{
+    const double glo = gate_lower(clamp, gate_one_sided);
 #pragma omp parallel for schedule(static)
     for (size_t i = 0; i < n; ++i) {
         double g = orc_load(G, adt, i);
         double u = orc_load(U, adt, i);
         if (clamp > 0.0) {
-            g = fmin(fmax(g, -clamp), clamp);
+            g = fmin(fmax(g, glo), clamp);
             u = fmin(fmax(u, -clamp), clamp);
         }
         double sig = 1.0 / (1.0 + exp(-alpha * g));
@@ -614,16 +622,18 @@ void orc_combine_backward(int T, int k, int K, const void *y, int adt,
  * outside it; dG and dU are evaluated in double and stored in the activation
  * type, like the forward's intermediates. */
 void orc_swiglu_backward(size_t n, const void *G, const void *U, const void *dh, int adt,
-                         double clamp, double alpha, double up_offset, void *dG, void *dU)
+                         double clamp, double alpha, double up_offset, int gate_one_sided,
+                         void *dG, void *dU)
 {
+    const double glo = gate_lower(clamp, gate_one_sided);
 #pragma omp parallel for schedule(static)
     for (size_t i = 0; i < n; ++i) {
         double g = orc_load(G, adt, i), u = orc_load(U, adt, i), d = orc_load(dh, adt, i);
         double gp = g, up = u, gpass = 1.0, upass = 1.0;
         if (clamp > 0.0) {
-            gp = fmin(fmax(g, -clamp), clamp);
+            gp = fmin(fmax(g, glo), clamp);
             up = fmin(fmax(u, -clamp), clamp);
-            gpass = (g >= -clamp && g <= clamp) ? 1.0 : 0.0;
+            gpass = (g >= glo && g <= clamp) ? 1.0 : 0.0;
             upass = (u >= -clamp && u <= clamp) ? 1.0 : 0.0;
         }
         double sg = 1.0 / (1.0 + exp(-alpha * gp));
@@ -644,7 +654,7 @@ void orc_awq_swiglu_input_backward(int A, int K, int I, const void *values, int 
                                    const int32_t *uqw, const int32_t *uqz, const void *us,
                                    int sdt, const void *gbias, const void *ubias,
                                    double clamp, double alpha, double up_offset,
-                                   const void *dh, void *dvalues)
+                                   int gate_one_sided, const void *dh, void *dvalues)
 {
     size_t sz = (adt == ORC_F32 ? 4 : 2) * (size_t)A * I;
     void *G = malloc(sz), *U = malloc(sz), *dG = malloc(sz), *dU = malloc(sz);
@@ -652,7 +662,8 @@ void orc_awq_swiglu_input_backward(int A, int K, int I, const void *values, int 
     double *Wu = (double *)malloc(sizeof(double) * (size_t)K * I);
     orc_awq_project(A, K, I, values, adt, row_experts, E, g, gqw, gqz, gs, sdt, gbias, G, NULL);
     orc_awq_project(A, K, I, values, adt, row_experts, E, g, uqw, uqz, us, sdt, ubias, U, NULL);
-    orc_swiglu_backward((size_t)A * I, G, U, dh, adt, clamp, alpha, up_offset, dG, dU);
+    orc_swiglu_backward((size_t)A * I, G, U, dh, adt, clamp, alpha, up_offset, gate_one_sided,
+                        dG, dU);
     for (int e = 0; e < E; ++e) {
         if (!expert_has_rows(A, row_experts, e))
             continue;
@@ -789,7 +800,8 @@ int orc_moe_forward(const orc_moe_args *a)
                         a->gate_s, a->sdt, a->gate_b, G, NULL);
         orc_awq_project(A, H, I, values, a->adt, rex, E, a->group, a->up_qw, a->up_qz,
                         a->up_s, a->sdt, a->up_b, U, NULL);
-        orc_swiglu((size_t)A * I, G, U, a->adt, a->clamp, a->alpha, a->up_offset, h);
+        orc_swiglu((size_t)A * I, G, U, a->adt, a->clamp, a->alpha, a->up_offset,
+                   a->gate_one_sided, h);
         orc_awq_project(A, I, H, h, a->adt, rex, E, a->group, a->down_qw, a->down_qz,
                         a->down_s, a->sdt, a->down_b, y, NULL);
     } else {
@@ -803,7 +815,8 @@ int orc_moe_forward(const orc_moe_args *a)
                 memcpy((char *)U + (p * I + i) * ab, (char *)GU + (p * 2 * I + 2 * i + 1) * ab, ab);
             }
         free(GU);
-        orc_swiglu((size_t)A * I, G, U, a->adt, a->clamp, a->alpha, a->up_offset, h);
+        orc_swiglu((size_t)A * I, G, U, a->adt, a->clamp, a->alpha, a->up_offset,
+                   a->gate_one_sided, h);
         orc_mxfp4_project(A, I, H, h, a->adt, rex, E, a->dn_blocks, a->dn_scales,
                           a->dn_bias, y);
     }

@@ -80,7 +80,7 @@ void orc_awq_project(int A, int K, int N, const void *in, int adt,
 
 /* storage-rounded SwiGLU on n elements */
 void orc_swiglu(size_t n, const void *G, const void *U, int adt, double clamp,
-                double alpha, double up_offset, void *h);
+                double alpha, double up_offset, int gate_one_sided, void *h);
 
 /* ascending expert-ID combine: out [T,K] */
 void orc_combine(int T, int k, int K, const void *y, int adt,
@@ -111,7 +111,8 @@ void orc_combine_backward(int T, int k, int K, const void *y, int adt,
                           const void *dout, void *dy, float *dweights);
 /* SwiGLU VJP at the forward's G, U: dG, dU [n] adt */
 void orc_swiglu_backward(size_t n, const void *G, const void *U, const void *dh, int adt,
-                         double clamp, double alpha, double up_offset, void *dG, void *dU);
+                         double clamp, double alpha, double up_offset, int gate_one_sided,
+                         void *dG, void *dU);
 /* input VJP of the gate/up + SwiGLU part: dvalues [A,K] adt from dh [A,I] adt */
 void orc_awq_swiglu_input_backward(int A, int K, int I, const void *values, int adt,
                                    const uint32_t *row_experts, int E, int g,
@@ -119,7 +120,7 @@ void orc_awq_swiglu_input_backward(int A, int K, int I, const void *values, int 
                                    const int32_t *uqw, const int32_t *uqz, const void *us,
                                    int sdt, const void *gbias, const void *ubias,
                                    double clamp, double alpha, double up_offset,
-                                   const void *dh, void *dvalues);
+                                   int gate_one_sided, const void *dh, void *dvalues);
 
 /* MXFP4 bank */
 double orc_e2m1_value(int nibble);
@@ -150,6 +151,7 @@ typedef struct {
     const uint8_t *gu_blocks, *gu_scales, *dn_blocks, *dn_scales;
     const uint16_t *gu_bias, *dn_bias;
     double clamp, alpha, up_offset;
+    int gate_one_sided; /* 0: g and u clamped to [-c, c]; 1: g clamped from above only */
     void *out;          /* [T,H] adt */
     /* optional intermediates for inspection (nullable) */
     uint32_t *selected; float *weights; int32_t *offsets, *row_src, *slot_pos;

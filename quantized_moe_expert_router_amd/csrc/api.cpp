@@ -179,6 +179,11 @@ bool unsorted_layout(int32_t rows, int32_t experts, int32_t K, int32_t N, int ac
     return true;
 }
 
+// Lower clamp bound of the gate: -clamp, or -inf for the one-sided variant.
+float gate_lower(const moeq_swiglu &fn) {
+    return fn.gate_one_sided ? -__builtin_inff() : -fn.clamp;
+}
+
 PackedOperand operand_of(const moeq_experts *w) {
     PackedOperand o;
     o.format = w->format;
@@ -339,7 +344,8 @@ moeq_status awq_grouped_swiglu(const moeq_route *route, const void *values, moeq
         I = gate->out_features;
     }
     if (act == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 activations are not implemented");
-    if (!(fn.clamp >= 0.0f) || !(fn.alpha == fn.alpha) || !(fn.up_offset == fn.up_offset))
+    if (!(fn.clamp >= 0.0f) || !(fn.alpha == fn.alpha) || !(fn.up_offset == fn.up_offset) ||
+        (fn.gate_one_sided != 0 && fn.gate_one_sided != 1))
         return fail(MOEQ_EINVAL, "bad SwiGLU parameters");
     const int A = route->T * route->top_k;
     if (A == 0) return MOEQ_OK;
@@ -359,6 +365,7 @@ moeq_status awq_grouped_swiglu(const moeq_route *route, const void *values, moeq
     p.w1 = bank ? p.w0 : operand_of(up);
     p.mode = bank ? PROJ_BANK_SWIGLU : PROJ_SWIGLU;
     p.clamp = fn.clamp;
+    p.gate_lo = gate_lower(fn);
     p.alpha = fn.alpha;
     p.up_offset = fn.up_offset;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -534,7 +541,8 @@ moeq_status awq_swiglu_input_backward(const moeq_route *route, const void *value
     if ((up->bias == nullptr) != (gate->bias == nullptr))
         return fail(MOEQ_EINVAL, "gate and up must both have or both lack a bias");
     if (act == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 activations are not implemented");
-    if (!(fn.clamp >= 0.0f) || !(fn.alpha == fn.alpha) || !(fn.up_offset == fn.up_offset))
+    if (!(fn.clamp >= 0.0f) || !(fn.alpha == fn.alpha) || !(fn.up_offset == fn.up_offset) ||
+        (fn.gate_one_sided != 0 && fn.gate_one_sided != 1))
         return fail(MOEQ_EINVAL, "bad SwiGLU parameters");
     const int A = route->T * route->top_k;
     const size_t need = awq_swiglu_input_backward_workspace_bytes(A, I, act);
@@ -581,6 +589,7 @@ moeq_status awq_swiglu_input_backward(const moeq_route *route, const void *value
     q.w1 = operand_of(up);
     q.mode = PROJ_SWIGLU;
     q.clamp = fn.clamp;
+    q.gate_lo = gate_lower(fn);
     q.alpha = fn.alpha;
     q.up_offset = fn.up_offset;
     bool fused = false;
@@ -602,8 +611,8 @@ moeq_status awq_swiglu_input_backward(const moeq_route *route, const void *value
         if ((st = device_status(err, "gate/up recompute")) != MOEQ_OK) return st;
     }
     if (!fused &&
-        (st = device_status(launch_swiglu_vjp(gg, uu, dh, act, (size_t)A * I, fn.clamp, fn.alpha,
-                                              fn.up_offset, s),
+        (st = device_status(launch_swiglu_vjp(gg, uu, dh, act, (size_t)A * I, fn.clamp,
+                                              gate_lower(fn), fn.alpha, fn.up_offset, s),
                             "SwiGLU VJP")) != MOEQ_OK)
         return st;
     // grad_values = dG . Wg^T + dU . Wu^T

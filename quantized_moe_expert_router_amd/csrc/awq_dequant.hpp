@@ -65,9 +65,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 // SwiGLU for bf16 outputs: the hardware exp and reciprocal (about one fp32 ulp
 // each) stay far inside the bf16 rounding of h.
-__device__ __forceinline__ float swiglu_f(float g, float u, float clamp, float alpha, float off) {
+// glo: the gate's lower clamp bound (-clamp, or -inf for the one-sided variant).
+__device__ __forceinline__ float swiglu_f(float g, float u, float clamp, float glo, float alpha,
+                                          float off) {
     if (clamp > 0.0f) {
-        g = fminf(fmaxf(g, -clamp), clamp);
+        g = fminf(fmaxf(g, glo), clamp);
         u = fminf(fmaxf(u, -clamp), clamp);
     }
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-alpha * g)) * (u + off);
@@ -77,13 +79,13 @@ __device__ __forceinline__ float swiglu_f(float g, float u, float clamp, float a
 // (bf16 outputs; hardware exp and reciprocal as in swiglu_f): g', u' clamped
 // when clamp > 0, a clamped value passing the derivative on the closed interval
 // and blocking it outside.
-__device__ __forceinline__ void swiglu_vjp_f(float g, float u, float d, float clamp, float alpha,
-                                             float off, float *dg, float *du) {
+__device__ __forceinline__ void swiglu_vjp_f(float g, float u, float d, float clamp, float glo,
+                                             float alpha, float off, float *dg, float *du) {
     float gpass = 1.0f, upass = 1.0f;
     if (clamp > 0.0f) {
-        gpass = (g >= -clamp && g <= clamp) ? 1.0f : 0.0f;
+        gpass = (g >= glo && g <= clamp) ? 1.0f : 0.0f;
         upass = (u >= -clamp && u <= clamp) ? 1.0f : 0.0f;
-        g = fminf(fmaxf(g, -clamp), clamp);
+        g = fminf(fmaxf(g, glo), clamp);
         u = fminf(fmaxf(u, -clamp), clamp);
     }
     const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-alpha * g));

@@ -147,7 +147,8 @@ __global__ __launch_bounds__(256) void weights_backward_kernel(
 template <int ACT>
 __global__ __launch_bounds__(256) void swiglu_vjp_kernel(void *__restrict__ G, void *__restrict__ U,
                                                          const void *__restrict__ dh, size_t n,
-                                                         float clamp, float alpha, float off) {
+                                                         float clamp, float glo, float alpha,
+                                                         float off) {
     typedef typename Storage<ACT>::T S;
     constexpr int VEC = 16 / sizeof(S);
     typedef S sv __attribute__((ext_vector_type(VEC)));
@@ -164,9 +165,9 @@ __global__ __launch_bounds__(256) void swiglu_vjp_kernel(void *__restrict__ G, v
         const float d = (float)dv[v];
         float gpass = 1.0f, upass = 1.0f;
         if (clamp > 0.0f) {
-            gpass = (g >= -clamp && g <= clamp) ? 1.0f : 0.0f;
+            gpass = (g >= glo && g <= clamp) ? 1.0f : 0.0f;
             upass = (u >= -clamp && u <= clamp) ? 1.0f : 0.0f;
-            g = fminf(fmaxf(g, -clamp), clamp);
+            g = fminf(fmaxf(g, glo), clamp);
             u = fminf(fmaxf(u, -clamp), clamp);
         }
         const float sg = ACT == MOEQ_F32 ? 1.0f / (1.0f + expf(-alpha * g))
@@ -181,20 +182,20 @@ __global__ __launch_bounds__(256) void swiglu_vjp_kernel(void *__restrict__ G, v
 }  // namespace
 
 hipError_t launch_swiglu_vjp(void *G, void *U, const void *dh, int act, size_t n, float clamp,
-                             float alpha, float up_offset, hipStream_t s) {
+                             float gate_lo, float alpha, float up_offset, hipStream_t s) {
     if (n == 0) return hipSuccess;
     const size_t vec = act == MOEQ_F32 ? 4 : 8;  // n % 8 == 0: whole vectors
     const size_t threads = n / vec;
     const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
     if (act == MOEQ_F32)
         hipLaunchKernelGGL((swiglu_vjp_kernel<MOEQ_F32>), grid, block, 0, s, G, U, dh, n, clamp,
-                           alpha, up_offset);
+                           gate_lo, alpha, up_offset);
     else if (act == MOEQ_BF16)
         hipLaunchKernelGGL((swiglu_vjp_kernel<MOEQ_BF16>), grid, block, 0, s, G, U, dh, n, clamp,
-                           alpha, up_offset);
+                           gate_lo, alpha, up_offset);
     else
         hipLaunchKernelGGL((swiglu_vjp_kernel<MOEQ_F16>), grid, block, 0, s, G, U, dh, n, clamp,
-                           alpha, up_offset);
+                           gate_lo, alpha, up_offset);
     return hipGetLastError();
 }
 

@@ -49,9 +49,10 @@ __device__ __forceinline__ float bias_value(const PackedOperand &w, int e, int n
     return load_f<SD>(w.bias, (size_t)e * w.N + n);
 }
 
-__device__ __forceinline__ float swiglu(float g, float u, float clamp, float alpha, float off) {
+__device__ __forceinline__ float swiglu(float g, float u, float clamp, float glo, float alpha,
+                                        float off) {
     if (clamp > 0.0f) {
-        g = fminf(fmaxf(g, -clamp), clamp);
+        g = fminf(fmaxf(g, glo), clamp);
         u = fminf(fmaxf(u, -clamp), clamp);
     }
     return g * (1.0f / (1.0f + expf(-alpha * g))) * (u + off);
@@ -131,11 +132,11 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(ProjProblem p) {
             } else if (MODE == PROJ_SWIGLU) {
                 const float g = round_to<ACT>(acc0[i] + bias_value<SD>(p.w0, e, col));
                 const float u = round_to<ACT>(acc1[i] + bias_value<SD>(p.w1, e, col));
-                v = swiglu(g, u, p.clamp, p.alpha, p.up_offset);
+                v = swiglu(g, u, p.clamp, p.gate_lo, p.alpha, p.up_offset);
             } else if (MODE == PROJ_BANK_SWIGLU) {
                 const float g = round_to<ACT>(acc0[i] + bias_value<SD>(p.w0, e, 2 * col));
                 const float u = round_to<ACT>(acc1[i] + bias_value<SD>(p.w0, e, 2 * col + 1));
-                v = swiglu(g, u, p.clamp, p.alpha, p.up_offset);
+                v = swiglu(g, u, p.clamp, p.gate_lo, p.alpha, p.up_offset);
             } else if (MODE == PROJ_INPUT_VJP2) {
                 v = acc0[i] + acc1[i];  // gate part, then up part
             } else {

@@ -52,6 +52,7 @@ struct StreamArgs {
     const void *sc[2];
     const void *bias[2];
     float clamp, alpha, up_offset;
+    float gate_lo;  // lower clamp bound of the gate
     const __bf16 *dh;  // backward epilogue: [A, N] derivative of h (NULL: forward)
     __bf16 *out2;      // backward epilogue: dU (out holds dG)
 };
@@ -324,13 +325,13 @@ void awq_stream_kernel(StreamArgs a) {
                             if constexpr (BWD) {  // backward: dG, dU at the rounded G, U
                                 const size_t at = (size_t)row * N + col;
                                 float dg, du;
-                                swiglu_vjp_f(gv, uv, (float)a.dh[at], a.clamp, a.alpha,
+                                swiglu_vjp_f(gv, uv, (float)a.dh[at], a.clamp, a.gate_lo, a.alpha,
                                              a.up_offset, &dg, &du);
                                 a.out[at] = (__bf16)dg;
                                 a.out2[at] = (__bf16)du;
                                 continue;
                             }
-                            v = swiglu_f(gv, uv, a.clamp, a.alpha, a.up_offset);
+                            v = swiglu_f(gv, uv, a.clamp, a.gate_lo, a.alpha, a.up_offset);
                         } else {
                             v = acc[sl][rt][i] + b0;
                         }
@@ -412,6 +413,7 @@ hipError_t run_stream(const ProjProblem &p, hipStream_t s) {
         a.bias[i] = ops[i]->bias;
     }
     a.clamp = p.clamp;
+    a.gate_lo = p.gate_lo;
     a.alpha = p.alpha;
     a.up_offset = p.up_offset;
     a.dh = static_cast<const __bf16 *>(p.in2);

@@ -64,6 +64,7 @@ struct MxArgs {
     int E, K, R, Nout;
     int nblk;  // blocks per m-tile
     float clamp, alpha, up_offset;
+    float gate_lo;  // lower clamp bound of the gate
 };
 
 __device__ __forceinline__ float e8m0_scale(uint32_t b) {
@@ -279,7 +280,7 @@ void mx_wave_kernel(MxArgs a) {
                     const int row = m0 + rt * 16 + grp * 4 + (gate_lane ? q : 2 + q);
                     if (row < m1 && r < R)
                         a.out[(size_t)row * a.Nout + f] =
-                            (__bf16)swiglu_f(gv, uv, a.clamp, a.alpha, a.up_offset);
+                            (__bf16)swiglu_f(gv, uv, a.clamp, a.gate_lo, a.alpha, a.up_offset);
                 }
             }
         } else {
@@ -328,6 +329,7 @@ hipError_t launch_mx(const ProjProblem &p, hipStream_t s) {
     a.R = p.w0.N;
     a.Nout = p.Nout;
     a.clamp = p.clamp;
+    a.gate_lo = p.gate_lo;
     a.alpha = p.alpha;
     a.up_offset = p.up_offset;
     const int rows_per_block = kWaves * kCT * 16;

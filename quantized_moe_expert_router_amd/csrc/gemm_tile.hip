@@ -64,6 +64,7 @@ struct TileArgs {
     const void *sc[2];
     const void *bias[2];
     float clamp, alpha, up_offset;
+    float gate_lo;  // lower clamp bound of the gate
 };
 
 template <int FMT, int NSETS, int SD>
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(256, 2) void awq_tile_kernel(TileArgs a) {
                 if (NSETS == 2) {
                     const float gv = round_to<MOEQ_BF16>(acc[rt][ct][i] + b0);
                     const float uv = round_to<MOEQ_BF16>(acc[rt][ct + 4][i] + b1);
-                    v = swiglu_f(gv, uv, a.clamp, a.alpha, a.up_offset);
+                    v = swiglu_f(gv, uv, a.clamp, a.gate_lo, a.alpha, a.up_offset);
                 } else {
                     v = acc[rt][ct][i] + b0;
                 }
@@ -342,6 +343,7 @@ hipError_t run_tile(const ProjProblem &p, const int32_t *tile_offsets, const int
         a.bias[i] = ops[i]->bias;
     }
     a.clamp = p.clamp;
+    a.gate_lo = p.gate_lo;
     a.alpha = p.alpha;
     a.up_offset = p.up_offset;
     // m-tiles are at most ceil(A / 128) + E; blocks past the last tile exit

@@ -69,6 +69,7 @@ struct WaveArgs {
     const void *sc[2];
     const void *bias[2];
     float clamp, alpha, up_offset;
+    float gate_lo;  // lower clamp bound of the gate
     const __bf16 *dh;  // backward epilogue: [A, Nout] derivative of h (NULL: forward)
     __bf16 *out2;      // backward epilogue: dU (out holds dG)
 };
@@ -302,7 +303,7 @@ void awq_wave_kernel(WaveArgs a) {
                     float dg[4], du[4];
 #pragma unroll
                     for (int s4 = 0; s4 < 4; ++s4)
-                        swiglu_vjp_f(gvv[s4][i], uvv[s4][i], dv[s4], a.clamp, a.alpha,
+                        swiglu_vjp_f(gvv[s4][i], uvv[s4][i], dv[s4], a.clamp, a.gate_lo, a.alpha,
                                      a.up_offset, &dg[s4], &du[s4]);
                     uint32_t *o = reinterpret_cast<uint32_t *>(a.out + at);
                     uint32_t *o2 = reinterpret_cast<uint32_t *>(a.out2 + at);
@@ -326,7 +327,7 @@ void awq_wave_kernel(WaveArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float gv = round_to<MOEQ_BF16>(acc[s4][rt][i] + bias_v[s4]);
-                    hv[i][s4] = swiglu_f(gv, uv[i], a.clamp, a.alpha, a.up_offset);
+                    hv[i][s4] = swiglu_f(gv, uv[i], a.clamp, a.gate_lo, a.alpha, a.up_offset);
                 }
             }
 #pragma unroll
@@ -382,6 +383,7 @@ hipError_t run_wave(const ProjProblem &p, hipStream_t s) {
         a.bias[i] = ops[i]->bias;
     }
     a.clamp = p.clamp;
+    a.gate_lo = p.gate_lo;
     a.alpha = p.alpha;
     a.up_offset = p.up_offset;
     a.dh = static_cast<const __bf16 *>(p.in2);

@@ -68,6 +68,7 @@ struct WsArgs {
     const void *sc[2];
     const void *bias[2];
     float clamp, alpha, up_offset;
+    float gate_lo;  // lower clamp bound of the gate
     const __bf16 *dh;  // backward epilogue: [A, Nout] derivative of h (NULL: forward)
     __bf16 *out2;      // backward epilogue: dU (out holds dG)
 };
@@ -313,13 +314,13 @@ void awq_ws_kernel(WsArgs a) {
                     if (a.dh) {  // backward: dG, dU at the rounded G, U
                         const size_t at = (size_t)row * a.Nout + n;
                         float dg, du;
-                        swiglu_vjp_f(gv, uv, (float)a.dh[at], a.clamp, a.alpha, a.up_offset,
+                        swiglu_vjp_f(gv, uv, (float)a.dh[at], a.clamp, a.gate_lo, a.alpha, a.up_offset,
                                      &dg, &du);
                         a.out[at] = (__bf16)dg;
                         a.out2[at] = (__bf16)du;
                         continue;
                     }
-                    v = swiglu_f(gv, uv, a.clamp, a.alpha, a.up_offset);
+                    v = swiglu_f(gv, uv, a.clamp, a.gate_lo, a.alpha, a.up_offset);
                 } else {
                     v = acc[rt][t][i] + b0;
                 }
@@ -352,6 +353,7 @@ hipError_t run_ws(const ProjProblem &p, hipStream_t s) {
         a.bias[i] = ops[i]->bias;
     }
     a.clamp = p.clamp;
+    a.gate_lo = p.gate_lo;
     a.alpha = p.alpha;
     a.up_offset = p.up_offset;
     a.dh = static_cast<const __bf16 *>(p.in2);

@@ -46,6 +46,7 @@ struct ProjProblem {
     PackedOperand w1;    // up (AWQ gate/up only)
     int mode;            // see ProjMode
     float clamp, alpha, up_offset;
+    float gate_lo;       // lower clamp bound of the gate: -clamp, or -inf (one-sided variant)
 };
 
 enum ProjMode {
@@ -85,7 +86,7 @@ hipError_t launch_combine_backward(const void *y, int act, const float *weights,
                                    const int32_t *slot_pos, const void *grad, int T, int k, int K,
                                    void *grad_y, float *grad_weights, hipStream_t s);
 hipError_t launch_swiglu_vjp(void *G, void *U, const void *dh, int act, size_t n, float clamp,
-                             float alpha, float up_offset, hipStream_t s);
+                             float gate_lo, float alpha, float up_offset, hipStream_t s);
 bool vjp_fits(const ProjProblem &p);
 hipError_t launch_vjp(const ProjProblem &p, hipStream_t s);
 hipError_t launch_weights_backward(const uint32_t *selected, const float *weights,

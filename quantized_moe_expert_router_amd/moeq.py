@@ -60,7 +60,8 @@ class Experts(C.Structure):
 
 
 class SwiGLU(C.Structure):
-    _fields_ = [("clamp", C.c_float), ("alpha", C.c_float), ("up_offset", C.c_float)]
+    _fields_ = [("clamp", C.c_float), ("alpha", C.c_float), ("up_offset", C.c_float),
+                ("gate_one_sided", C.c_int32)]
 
 
 _lib = None
@@ -257,7 +258,8 @@ def moe_dispatch_counts(route: RouteState, expert_prefix: Sequence[int]) -> list
 
 def awq_grouped_swiglu(route: RouteState, values: torch.Tensor, gate, up=None,
                        clamp: float = 0.0, alpha: float = 1.0, up_offset: float = 0.0,
-                       h: Optional[torch.Tensor] = None) -> torch.Tensor:
+                       h: Optional[torch.Tensor] = None,
+                       gate_one_sided: bool = False) -> torch.Tensor:
     gc = gate.c()
     uc = None if up is None else up.c()
     I = gc.out_features // 2 if isinstance(gate, Mxfp4Bank) else gc.out_features
@@ -265,7 +267,8 @@ def awq_grouped_swiglu(route: RouteState, values: torch.Tensor, gate, up=None,
         h = torch.empty(values.shape[0], I, dtype=values.dtype, device=values.device)
     _check(lib().awq_grouped_swiglu(C.byref(route.c), _ptr(values), _dt(values), C.byref(gc),
                                     None if uc is None else C.byref(uc),
-                                    SwiGLU(clamp, alpha, up_offset), _ptr(h),
+                                    SwiGLU(clamp, alpha, up_offset, int(gate_one_sided)),
+                                    _ptr(h),
                                     _stream(values.device)))
     return h
 
@@ -357,7 +360,8 @@ def awq_swiglu_input_backward(route: RouteState, values: torch.Tensor, gate: Awq
                               up: AwqExperts, down: AwqExperts, grad: torch.Tensor,
                               clamp: float = 0.0, alpha: float = 1.0, up_offset: float = 0.0,
                               workspace: Optional[torch.Tensor] = None,
-                              grad_values: Optional[torch.Tensor] = None) -> torch.Tensor:
+                              grad_values: Optional[torch.Tensor] = None,
+                              gate_one_sided: bool = False) -> torch.Tensor:
     """Input VJP through down, SwiGLU and gate/up (first order): [A, K] act."""
     gc, uc, dc = gate.c(), up.c(), down.c()
     A = values.shape[0]
@@ -368,7 +372,8 @@ def awq_swiglu_input_backward(route: RouteState, values: torch.Tensor, gate: Awq
         grad_values = torch.empty_like(values)
     _check(lib().awq_swiglu_input_backward(C.byref(route.c), _ptr(values), _dt(values),
                                            C.byref(gc), C.byref(uc), C.byref(dc),
-                                           SwiGLU(clamp, alpha, up_offset), _ptr(grad),
+                                           SwiGLU(clamp, alpha, up_offset,
+                                                  int(gate_one_sided)), _ptr(grad),
                                            _ptr(grad_values), _ptr(workspace),
                                            workspace.numel(), _stream(values.device)))
     return grad_values
@@ -435,9 +440,11 @@ def frozen_awq_forward(x: torch.Tensor, w, y: Optional[torch.Tensor] = None,
     return y
 
 
-def moe_ffn(x, logits, expert_bias, top_k, gate, up, down, clamp=0.0, alpha=1.0, up_offset=0.0):
+def moe_ffn(x, logits, expert_bias, top_k, gate, up, down, clamp=0.0, alpha=1.0, up_offset=0.0,
+            gate_one_sided=False):
     """The whole forward path: dispatch -> gate/up + SwiGLU -> down -> combine."""
     d = moe_dispatch(x, logits, expert_bias, top_k)
-    h = awq_grouped_swiglu(d["route"], d["values"], gate, up, clamp, alpha, up_offset)
+    h = awq_grouped_swiglu(d["route"], d["values"], gate, up, clamp, alpha, up_offset,
+                           gate_one_sided=gate_one_sided)
     y = awq_grouped_down(d["route"], h, down)
     return moe_combine(d["route"], y, d["weights"]), d

@@ -30,7 +30,8 @@ def run_path(p, d=None):
     disp = moeq.moe_dispatch(d["x"], d["logits"], d["router_bias"], p["k"])
     r = disp["route"]
     h = moeq.awq_grouped_swiglu(r, disp["values"], d["gate"], d["up_arg"], p["clamp"],
-                                p["alpha"], p["up_offset"])
+                                p["alpha"], p["up_offset"],
+                                gate_one_sided=p.get("gate_one_sided", False))
     y = moeq.awq_grouped_down(r, h, d["down"])
     out = moeq.moe_combine(r, y, disp["weights"])
     torch.cuda.synchronize()

@@ -152,6 +152,8 @@ def test_projection_validation(L):
     assert swiglu(L, r, awq(), awq(), act=moeq.F16) == moeq.EUNSUPPORTED
     assert swiglu(L, r, awq(), awq(), act=5) == moeq.EDTYPE
     assert swiglu(L, r, awq(), awq(), fn=(-1.0, 1.0, 0.0)) == moeq.EINVAL
+    assert swiglu(L, r, awq(), awq(), fn=(7.0, 1.702, 1.0, 1)) == moeq.OK   # one-sided gate
+    assert swiglu(L, r, awq(), awq(), fn=(7.0, 1.702, 1.0, 2)) == moeq.EINVAL
     # MXFP4 banks (native.rs): the gate/up role requires an interleaved bank with bias
     assert swiglu(L, r, bank(), None) == moeq.OK
     assert swiglu(L, r, bank(inter=0), None) == moeq.ESHAPE

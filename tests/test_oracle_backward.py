@@ -178,3 +178,32 @@ def test_swiglu_input_backward_linear_case_is_two_matmuls(orc):
     Wu = orc.awq_dequant(*up[:3], "f16", cfg.group)
     ref = np.stack([dG[p] @ Wg[rex[p]].T + dU[p] @ Wu[rex[p]].T for p in range(v.shape[0])])
     np.testing.assert_allclose(dv, ref, rtol=1e-6, atol=1e-6)
+
+
+def test_swiglu_one_sided_gate_clamp(orc):
+    """The variant some MXFP4 models use (gate clamped from above only, alpha 1.702,
+    up + 1): closed form in float64, and its derivatives by central differences."""
+    c, alpha, off = 7.0, 1.702, 1.0
+    g = np.array([-20.0, -7.5, -3.0, 0.0, 3.0, 7.0, 9.0, -9.0], np.float32)
+    u = np.array([2.0, -9.0, 8.0, 1.0, -2.0, 3.0, 0.5, -6.0], np.float32)
+    h = orc.swiglu(g, u, "f32", clamp=c, alpha=alpha, up_offset=off, gate_one_sided=True)
+    gp = np.minimum(g.astype(np.float64), c)
+    up = np.clip(u.astype(np.float64), -c, c)
+    ref = gp * sp.expit(alpha * gp) * (up + off)
+    np.testing.assert_allclose(h, ref, rtol=1e-6, atol=1e-30)
+    two = orc.swiglu(g, u, "f32", clamp=c, alpha=alpha, up_offset=off)
+    assert h[0] != two[0] and h[3] == two[3]      # only the gate's lower clamp differs
+    d = np.ones_like(g)
+    dG, dU = orc.swiglu_backward(g, u, d, "f32", clamp=c, alpha=alpha, up_offset=off,
+                                 gate_one_sided=True)
+    eps = 1e-6
+
+    def hf(gg, uu):
+        gg, uu = np.minimum(gg, c), np.clip(uu, -c, c)
+        return gg * sp.expit(alpha * gg) * (uu + off)
+    g64, u64 = g.astype(np.float64), u.astype(np.float64)
+    inside = g64 < c - 1e-3                                   # away from the kink at c
+    fdg = (hf(g64 + eps, u64) - hf(g64 - eps, u64)) / (2 * eps)
+    np.testing.assert_allclose(dG[inside], fdg[inside], rtol=1e-5, atol=1e-7)
+    assert dG[6] == 0.0 and dG[0] != 0.0                      # above c: blocked; below -c: not
+    assert dU[1] == 0.0                                       # u beyond the clamp: blocked
