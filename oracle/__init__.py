@@ -73,6 +73,10 @@ def _load():
     lib.orc_e8m0_value.argtypes = [i32]
     lib.orc_mxfp4_dequant.argtypes = [i32, i32, i32, vp, vp, vp]
     lib.orc_mxfp4_project.argtypes = [i32, i32, i32, vp, i32, vp, i32, vp, vp, vp, vp]
+    lib.orc_e4m3_value.restype = C.c_double
+    lib.orc_e4m3_value.argtypes = [i32]
+    lib.orc_mxfp8_quantize.argtypes = [i32, i32, vp, i32, vp, vp]
+    lib.orc_mx8_project.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp, vp, i32, vp]
     lib.orc_moe_forward.restype = C.c_int
     lib.orc_moe_forward.argtypes = [vp]
     _lib = lib
@@ -348,6 +352,38 @@ def mxfp4_project(x, adt, row_experts, blocks, scales, bias_bf16):
     out = np.zeros((A, R), NP_STORAGE[adt])
     _load().orc_mxfp4_project(A, Cin, R, _p(x), DT[adt], _p(rex), E, _p(blocks), _p(scales),
                               _p(b), _p(out))
+    return out
+
+
+# ---------------------------------------------------------------- MXFP8 activations
+def e4m3_value(byte: int) -> float:
+    return float(_load().orc_e4m3_value(int(byte)))
+
+
+def mxfp8_quantize(x, adt):
+    """OCP MX quantization of 32-element row blocks: (codes u8 [rows, K], scales u8 [rows, K/32])."""
+    x = _store(x, adt)
+    rows, K = x.shape
+    q = np.zeros((rows, K), np.uint8)
+    s = np.zeros((rows, K // 32), np.uint8)
+    _load().orc_mxfp8_quantize(rows, K, _p(x), DT[adt], _p(q), _p(s))
+    return q, s
+
+
+def mx8_project(q, s, row_experts, blocks, scales, bias_bf16, adt):
+    """Projection of MXFP8 rows with an MXFP4 bank, output rounded to adt."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint8)
+    blocks = _c(blocks, np.uint8)
+    scales = _c(scales, np.uint8)
+    E, R, NB, sixteen = blocks.shape
+    A, C_ = q.shape
+    assert NB * 32 == C_
+    rex = None if row_experts is None else _c(row_experts, np.uint32)
+    b = None if bias_bf16 is None else _c(bias_bf16, np.uint16)
+    out = np.zeros((A, R), NP_STORAGE[adt])
+    _load().orc_mx8_project(A, C_, R, _p(q), _p(s), _p(rex), E, _p(blocks), _p(scales), _p(b),
+                            DT[adt], _p(out))
     return out
 
 

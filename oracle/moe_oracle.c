@@ -770,6 +770,111 @@ void orc_mxfp4_project(int A, int C, int R, const void *in, int adt,
 }
 
 /* ------------------------------------------------------------------ */
+/* MXFP8 activations (the block-scaled MFMA variant of the MXFP4 bank)  */
+/* ------------------------------------------------------------------ */
+
+/* OCP Microscaling FP8 E4M3 element: sign bit 7, exponent bits 6..3 (bias 7),
+ * mantissa bits 2..0; exponent 0 is subnormal (mantissa/8 * 2^-6); S.1111.111 is
+ * NaN, so the largest finite magnitude is 1.75 * 2^8 = 448. */
+double orc_e4m3_value(int byte)
+{
+    int sign = (byte >> 7) & 1, ex = (byte >> 3) & 15, man = byte & 7;
+    if (ex == 15 && man == 7)
+        return NAN;
+    double v = ex == 0 ? ldexp(man / 8.0, -6) : ldexp(1.0 + man / 8.0, ex - 7);
+    return sign ? -v : v;
+}
+
+/* Nearest E4M3 code to v by scanning every finite non-negative code, ties to the
+ * even code (mantissa bit 0 clear); |v| beyond the largest code saturates to it.
+ * The sign is kept, zero included. */
+static uint8_t e4m3_round(double v)
+{
+    double a = fabs(v);
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double d = fabs(orc_e4m3_value(c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+            bd = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(best | (signbit(v) ? 0x80 : 0));
+}
+
+/* OCP MX quantization of each 32-element block of a row to MXFP8 (E4M3): the
+ * shared exponent is floor(log2(max |v|)) minus 8 (the largest E4M3 exponent),
+ * kept in the E8M0 range [-127, 127]; each element is v / 2^shared rounded to
+ * the nearest E4M3 value, ties to even, saturated to +-448.  A block of zeros
+ * gets scale byte 0 (2^-127) and zero elements.  x [rows, K] adt, K % 32 == 0;
+ * q [rows, K] codes, s [rows, K/32] scale bytes (shared + 127). */
+void orc_mxfp8_quantize(int rows, int K, const void *x, int adt, uint8_t *q, uint8_t *s)
+{
+    const int nb = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < rows; ++r)
+        for (int b = 0; b < nb; ++b) {
+            size_t base = (size_t)r * K + (size_t)b * 32;
+            double amax = 0.0;
+            for (int i = 0; i < 32; ++i)
+                amax = fmax(amax, fabs(orc_load(x, adt, base + i)));
+            int shared = -127;
+            if (amax > 0.0) {
+                int e2;
+                frexp(amax, &e2);   /* amax = f 2^e2, f in [0.5, 1): floor(log2) = e2 - 1 */
+                shared = e2 - 1 - 8;
+                if (shared < -127) shared = -127;
+                if (shared > 127) shared = 127;
+            }
+            s[(size_t)r * nb + b] = (uint8_t)(shared + 127);
+            for (int i = 0; i < 32; ++i)
+                q[base + i] = e4m3_round(ldexp(orc_load(x, adt, base + i), -shared));
+        }
+}
+
+/* The projection of MXFP8 rows with an MXFP4 bank, products exact:
+ *   out[p, r] = round_adt( sum_c e4m3(q[p,c]) 2^(s[p,c/32]-127) * W_e[r,c] + bias[e,r] )
+ * in double. */
+void orc_mx8_project(int A, int C, int R, const uint8_t *q, const uint8_t *s,
+                     const uint32_t *row_experts, int E, const uint8_t *blocks,
+                     const uint8_t *scales, const uint16_t *bias_bf16, int adt, void *out)
+{
+    const int nb = C / 32;
+    double *W = (double *)malloc(sizeof(double) * (size_t)R * C);
+    double *xv = (double *)malloc(sizeof(double) * (size_t)(A > 0 ? A : 1) * C);
+#pragma omp parallel for schedule(static)
+    for (int p = 0; p < A; ++p)
+        for (int c = 0; c < C; ++c)
+            xv[(size_t)p * C + c] = orc_e4m3_value(q[(size_t)p * C + c]) *
+                                    orc_e8m0_value(s[(size_t)p * nb + c / 32]);
+    for (int e = 0; e < E; ++e) {
+        if (!expert_has_rows(A, row_experts, e))
+            continue;
+#pragma omp parallel for schedule(static)
+        for (int r = 0; r < R; ++r)
+            for (int c = 0; c < C; ++c)
+                W[(size_t)r * C + c] = mxfp4_coeff(R, C, blocks, scales, e, r, c);
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int p = 0; p < A; ++p) {
+            int pe = row_experts ? (int)row_experts[p] : 0;
+            if (pe != e)
+                continue;
+            for (int r = 0; r < R; ++r) {
+                double acc = 0.0;
+                for (int c = 0; c < C; ++c)
+                    acc += xv[(size_t)p * C + c] * W[(size_t)r * C + c];
+                if (bias_bf16)
+                    acc += orc_bf16_value(bias_bf16[(size_t)e * R + r]);
+                orc_store(out, adt, (size_t)p * R + r, acc);
+            }
+        }
+    }
+    free(W);
+    free(xv);
+}
+
+/* ------------------------------------------------------------------ */
 /* whole forward path                                                   */
 /* ------------------------------------------------------------------ */
 

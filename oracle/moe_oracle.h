@@ -132,6 +132,13 @@ void orc_mxfp4_dequant(int E, int R, int C, const uint8_t *blocks,
 void orc_mxfp4_project(int A, int C, int R, const void *in, int adt,
                        const uint32_t *row_experts, int E, const uint8_t *blocks,
                        const uint8_t *scales, const uint16_t *bias_bf16, void *out);
+/* MXFP8 activations: E4M3 element value; OCP MX quantization of 32-blocks;
+ * projection of the quantized rows with an MXFP4 bank */
+double orc_e4m3_value(int byte);
+void orc_mxfp8_quantize(int rows, int K, const void *x, int adt, uint8_t *q, uint8_t *s);
+void orc_mx8_project(int A, int C, int R, const uint8_t *q, const uint8_t *s,
+                     const uint32_t *row_experts, int E, const uint8_t *blocks,
+                     const uint8_t *scales, const uint16_t *bias_bf16, int adt, void *out);
 
 /* Whole forward path, logits -> out, for the CPU baseline and end-to-end tests.
  * fmt 0 = AWQ (gate/up/down descriptors), fmt 1 = MXFP4 interleaved bank.
