@@ -17,6 +17,11 @@ expert IDs: local sort, grouped projection, inverse permutation) on the gate cub
 one row per assignment in token order -- the expert-parallel receive primitive.
 The call validates the IDs on the host, so it synchronises and runs eagerly.
 
+--path mx8 (MXFP4 workload only) times the same forward step with the bank on
+gfx950's block-scaled MFMA: mx8_grouped_swiglu / mx8_grouped_down quantize their
+input rows to MXFP8 and multiply them with the FP4 bank as stored -- an opt-in
+variant whose activations are rounded differently from the bf16 path.
+
 --path backward times the first-order backward path instead: one step =
 moe_combine_backward (expert rows + FP32 weights) -> awq_swiglu_input_backward
 (down VJP, recomputed gate/up with the SwiGLU VJP, both transposed cubes) ->
@@ -39,6 +44,8 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 METRIC = "MoE expert-FFN tokens/s at 1 GPU; % of HBM (decode) / MFMA (prefill) peak"
 METRIC_BWD = "MoE expert-FFN backward tokens/s at 1 GPU (first-order input VJPs)"
+METRIC_MX8 = "MoE expert-FFN tokens/s at 1 GPU, MXFP4 bank on the block-scaled MFMA (MXFP8 activations)"
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA (the fp8 x fp4 scaled MFMA's operand type)
 METRIC_UNSORTED = "unsorted-row expert projection rows/s at 1 GPU (gate cube, rows in token order)"
 
 
@@ -51,7 +58,8 @@ def parse():
                     choices=["tiny", "decode", "prefill", "many", "mxfp4"])
     ap.add_argument("--replica-bytes", type=float, default=1.2e9,
                     help="weight bytes cycled through by consecutive steps")
-    ap.add_argument("--path", default="forward", choices=["forward", "backward", "unsorted"])
+    ap.add_argument("--path", default="forward",
+                    choices=["forward", "backward", "unsorted", "mx8"])
     ap.add_argument("--eager", action="store_true", help="no HIP graph capture")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -273,12 +281,30 @@ def main():
     y = torch.empty(A, H, dtype=adt, device=dev)
     out = torch.empty(T, H, dtype=adt, device=dev)
 
+    mx8 = args.path == "mx8"
+    if mx8 and cfg.fmt != "mxfp4":
+        print("--path mx8 runs the MXFP4 bank workload (--config mxfp4)", file=sys.stderr)
+        sys.exit(2)
+    if mx8:
+        wsm = torch.empty(moeq.lib().mx8_workspace_bytes(A, max(H, I)), dtype=torch.uint8,
+                          device=dev)
+
+    def gate_up(w):
+        if mx8:
+            moeq.mx8_grouped_swiglu(route, bufs["values"], w["gate"], cfg.clamp, 1.0, 0.0,
+                                    h=h, workspace=wsm)
+        else:
+            moeq.awq_grouped_swiglu(route, bufs["values"], w["gate"], w["up_arg"], cfg.clamp,
+                                    1.0, 0.0, h)
+
     def step(i):
         w = replicas[i % R]
         moeq.moe_dispatch(base["x"], base["logits"], base["router_bias"], k, route, bufs)
-        moeq.awq_grouped_swiglu(route, bufs["values"], w["gate"], w["up_arg"], cfg.clamp, 1.0,
-                                0.0, h)
-        moeq.awq_grouped_down(route, h, w["down"], y)
+        gate_up(w)
+        if mx8:
+            moeq.mx8_grouped_down(route, h, w["down"], y, workspace=wsm)
+        else:
+            moeq.awq_grouped_down(route, h, w["down"], y)
         moeq.moe_combine(route, y, bufs["weights"], out)
 
     if args.path == "unsorted":
@@ -409,8 +435,7 @@ def main():
         if backward:
             chain(w)
         else:
-            moeq.awq_grouped_swiglu(route, bufs["values"], w["gate"], w["up_arg"], cfg.clamp,
-                                    1.0, 0.0, h)
+            gate_up(w)
         b.record(stream)
     torch.cuda.synchronize()
     k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
@@ -454,7 +479,10 @@ def main():
     # the gate/up call's own bound: MFMA above the ridge point, else HBM
     gu_flops = 4 * A * p["H"] * p["I"]
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if gu_flops / ab["gateup"] > ridge:
+    if mx8:   # the fp8 x fp4 block-scaled MFMA: against the dense fp8 peak
+        bound, peak, unit = "mfma", FP8_PEAK_TFLOPS, "TFLOP/s"
+        achieved = gu_flops / (k_ms * 1e-3) / 1e12
+    elif gu_flops / ab["gateup"] > ridge:
         bound, peak, unit = "mfma", BF16_PEAK_TFLOPS, "TFLOP/s"
         achieved = gu_flops / (k_ms * 1e-3) / 1e12
     else:
@@ -464,14 +492,18 @@ def main():
     path_gbs = ab["total"] / (ms * 1e-3) / 1e9
     path_tflops = F / (ms * 1e-3) / 1e12
     res = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC_MX8 if mx8 else METRIC, "value": round(tok_s, 1), "unit": "tokens/s",
+        "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if cfg.adt == "bf16" else "f32", "data": "synthetic",
+        "dtype": "mxfp8xmxfp4" if mx8 else ("bf16" if cfg.adt == "bf16" else "f32"),
+        "data": "synthetic",
         "config": {"workload": workload_name(cfg), "tokens": T, "assignments": A,
                    "touched_experts": ab["touched"], "weight_replicas": R,
                    "graph": graphs is not None},
-        "roofline": {"kernel": "awq_grouped_swiglu (gate/up dequant-GEMM + SwiGLU)",
+        "roofline": {"kernel": ("mx8_grouped_swiglu (MXFP8 quantization + block-scaled "
+                                "MFMA gate/up + SwiGLU)") if mx8 else
+                               "awq_grouped_swiglu (gate/up dequant-GEMM + SwiGLU)",
                      "bound": bound, "achieved": round(achieved, 1), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic, "kernel_ms": round(k_ms, 5),

@@ -357,6 +357,37 @@ moeq_status frozen_awq_forward(const void *x, moeq_dtype act, int32_t rows,
                                const moeq_experts *w, void *y, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/*
+ * Block-scaled MFMA path of the MXFP4 bank (an opt-in variant: the activations
+ * are rounded differently from the bf16 path).  native.rs ExpertLayout::Native
+ * banks are read as they are by gfx950's v_mfma_scale_f32_16x16x128_f8f6f4; the
+ * activation rows are first quantized to OCP MXFP8: per 32-element block a
+ * shared E8M0 exponent floor(log2 max|v|) - 8 (kept in [-127, 127]; a zero block
+ * gets byte 0), elements v / 2^shared saturated to +-448 and rounded to the
+ * nearest E4M3 value, ties to even.  Products are exact, accumulation fp32.
+ *
+ * mx8_quantize: x [rows, K] bf16 (16-byte aligned, K % 32 == 0) -> q [rows, K] E4M3
+ *   codes, s [rows, K/32] E8M0 bytes.
+ * mx8_grouped_swiglu: as awq_grouped_swiglu over an interleaved gate/up bank,
+ *   with MXFP8 values: h = round_bf16(SwiGLU(round_bf16(G), round_bf16(U))).
+ * mx8_grouped_down: as awq_grouped_down over a plain bank, with MXFP8 h.
+ * Both take bf16 activations and a workspace (device, 256-byte aligned) of at
+ * least mx8_workspace_bytes(A, in_features) for the quantized rows; bank rows
+ * must be a multiple of 64 (else EUNSUPPORTED).
+ */
+size_t mx8_workspace_bytes(int32_t rows, int32_t K);
+
+moeq_status mx8_quantize(const void *x, moeq_dtype act, int32_t rows, int32_t K, uint8_t *q,
+                         uint8_t *s, void *stream);
+
+moeq_status mx8_grouped_swiglu(const moeq_route *route, const void *values, moeq_dtype act,
+                               const moeq_experts *gate_up, moeq_swiglu fn, void *h,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+moeq_status mx8_grouped_down(const moeq_route *route, const void *h, moeq_dtype act,
+                             const moeq_experts *down, void *y, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *moeq_status_string(moeq_status status);
 

@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(CSRC, "libmoeq.so")
 SOURCES = ["api.cpp", "route.hip", "gemm_generic.hip", "gemm_mfma.hip", "gemm_tile.hip", "gemm_wave.hip", "gemm_mx.hip", "gemm_ws.hip",
-           "backward.hip", "gemm_vjp.hip"]
+           "backward.hip", "gemm_vjp.hip",
+           "gemm_mx8.hip"]
 ARCH = os.environ.get("MOEQ_ARCH", "gfx950")
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

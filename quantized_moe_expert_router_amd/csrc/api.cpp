@@ -629,6 +629,98 @@ moeq_status awq_swiglu_input_backward(const moeq_route *route, const void *value
                          "gate/up input VJP");
 }
 
+// ---------------------------------------------------------------- MXFP8 activations
+
+size_t mx8_workspace_bytes(int32_t rows, int32_t K) {
+    if (rows < 0 || K < 32 || K % 32 != 0) return 0;
+    size_t n;
+    if (!mul_ok((size_t)rows, (size_t)K, &n)) return 0;
+    return align256(n ? n : 1) + align256(n / 32 ? n / 32 : 1);
+}
+
+moeq_status mx8_quantize(const void *x, moeq_dtype act, int32_t rows, int32_t K, uint8_t *q,
+                         uint8_t *s, void *stream) {
+    if (act != MOEQ_BF16) return fail(MOEQ_EUNSUPPORTED, "MXFP8 quantization takes bf16 rows");
+    if (rows < 0 || K < 32 || K % 32 != 0)
+        return fail(MOEQ_ESHAPE, "rows >= 0 and K a positive multiple of 32 (K = %d)", K);
+    if (rows == 0) return MOEQ_OK;
+    if (!x || !q || !s) return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    if ((uintptr_t)x % 16 != 0 || (uintptr_t)q % 16 != 0)
+        return fail(MOEQ_EINVAL, "rows must be 16-byte aligned");
+    return device_status(launch_mx8_quant(x, rows, K, q, s, static_cast<hipStream_t>(stream)),
+                         "MXFP8 quantization");
+}
+
+namespace {
+
+moeq_status mx8_check(const moeq_route *route, const void *in, moeq_dtype act,
+                      const moeq_experts *w, bool swiglu, void *workspace, size_t bytes) {
+    moeq_status st = check_route(route);
+    if (st != MOEQ_OK) return st;
+    if (!w) return fail(MOEQ_EINVAL, "bank descriptor is NULL");
+    if (w->format != MOEQ_FMT_MXFP4_BANK)
+        return fail(MOEQ_EUNSUPPORTED, "the block-scaled MFMA path takes MXFP4 banks");
+    if ((st = check_experts(w, swiglu ? "gate/up bank" : "down bank", route->E, -1, -1,
+                            swiglu)) != MOEQ_OK)
+        return st;
+    if (act != MOEQ_BF16) return fail(MOEQ_EUNSUPPORTED, "MXFP8 activations come from bf16 rows");
+    if (w->out_features % 64 != 0)
+        return fail(MOEQ_EUNSUPPORTED, "bank rows %d are not a multiple of 64", w->out_features);
+    const int A = route->T * route->top_k;
+    if (A == 0) return MOEQ_OK;
+    if (!in) return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    if (!workspace) return fail(MOEQ_EINVAL, "workspace is NULL");
+    if ((uintptr_t)workspace % 256 != 0)
+        return fail(MOEQ_EWORKSPACE, "workspace must be 256-byte aligned");
+    const size_t need = mx8_workspace_bytes(A, w->in_features);
+    if (bytes < need) return fail(MOEQ_EWORKSPACE, "workspace has %zu bytes, needs %zu", bytes, need);
+    return MOEQ_OK;
+}
+
+moeq_status mx8_run(const moeq_route *route, const void *in, const moeq_experts *w, bool swiglu,
+                    moeq_swiglu fn, void *out, void *workspace, hipStream_t s) {
+    const int A = route->T * route->top_k, K = w->in_features;
+    uint8_t *q = static_cast<uint8_t *>(workspace);
+    uint8_t *qs = q + align256((size_t)A * K);
+    moeq_status st;
+    if ((st = device_status(launch_mx8_quant(in, A, K, q, qs, s), "MXFP8 quantization")) !=
+        MOEQ_OK)
+        return st;
+    return device_status(launch_mx8_gemm(q, qs, A, K, operand_of(w), route->expert_offsets,
+                                         route->tile_offsets, route->tile_expert, route->E,
+                                         swiglu, swiglu ? w->out_features / 2 : w->out_features,
+                                         fn.clamp, gate_lower(fn), fn.alpha, fn.up_offset, out,
+                                         s),
+                         "block-scaled projection");
+}
+
+}  // namespace
+
+moeq_status mx8_grouped_swiglu(const moeq_route *route, const void *values, moeq_dtype act,
+                               const moeq_experts *gate_up, moeq_swiglu fn, void *h,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    moeq_status st = mx8_check(route, values, act, gate_up, true, workspace, workspace_bytes);
+    if (st != MOEQ_OK) return st;
+    if (!(fn.clamp >= 0.0f) || !(fn.alpha == fn.alpha) || !(fn.up_offset == fn.up_offset) ||
+        (fn.gate_one_sided != 0 && fn.gate_one_sided != 1))
+        return fail(MOEQ_EINVAL, "bad SwiGLU parameters");
+    if (route->T == 0) return MOEQ_OK;
+    if (!h) return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    return mx8_run(route, values, gate_up, true, fn, h, workspace,
+                   static_cast<hipStream_t>(stream));
+}
+
+moeq_status mx8_grouped_down(const moeq_route *route, const void *h, moeq_dtype act,
+                             const moeq_experts *down, void *y, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    moeq_status st = mx8_check(route, h, act, down, false, workspace, workspace_bytes);
+    if (st != MOEQ_OK) return st;
+    if (route->T == 0) return MOEQ_OK;
+    if (!y) return fail(MOEQ_EINVAL, "NULL tensor pointer");
+    return mx8_run(route, h, down, false, moeq_swiglu{0.0f, 1.0f, 0.0f, 0}, y, workspace,
+                   static_cast<hipStream_t>(stream));
+}
+
 // ---------------------------------------------------------------- unsorted rows
 
 size_t awq_expert_workspace_bytes(int32_t rows, int32_t experts, int32_t K, int32_t N,

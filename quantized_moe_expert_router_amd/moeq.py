@@ -31,6 +31,7 @@ EXPORTS = ("moeq_route_workspace_bytes", "moeq_route_bind", "moe_dispatch",
            "moe_dispatch_weights_backward", "awq_swiglu_input_backward_workspace_bytes",
            "awq_swiglu_input_backward", "awq_expert_workspace_bytes", "awq_expert_forward",
            "awq_expert_input_backward", "frozen_awq_workspace_bytes", "frozen_awq_forward",
+           "mx8_workspace_bytes", "mx8_quantize", "mx8_grouped_swiglu", "mx8_grouped_down",
            "moeq_status_string", "moeq_last_error")
 
 
@@ -121,6 +122,16 @@ def lib():
     L.frozen_awq_forward.restype = C.c_int
     L.frozen_awq_forward.argtypes = [vp, C.c_int, i32, C.POINTER(Experts), vp, vp, C.c_size_t,
                                      vp]
+    L.mx8_workspace_bytes.restype = C.c_size_t
+    L.mx8_workspace_bytes.argtypes = [i32, i32]
+    L.mx8_quantize.restype = C.c_int
+    L.mx8_quantize.argtypes = [vp, C.c_int, i32, i32, vp, vp, vp]
+    L.mx8_grouped_swiglu.restype = C.c_int
+    L.mx8_grouped_swiglu.argtypes = [C.POINTER(Route), vp, C.c_int, C.POINTER(Experts), SwiGLU,
+                                     vp, vp, C.c_size_t, vp]
+    L.mx8_grouped_down.restype = C.c_int
+    L.mx8_grouped_down.argtypes = [C.POINTER(Route), vp, C.c_int, C.POINTER(Experts), vp, vp,
+                                   C.c_size_t, vp]
     L.moeq_status_string.restype = C.c_char_p
     L.moeq_status_string.argtypes = [C.c_int]
     L.moeq_last_error.restype = C.c_char_p
@@ -437,6 +448,50 @@ def frozen_awq_forward(x: torch.Tensor, w, y: Optional[torch.Tensor] = None,
     workspace = _workspace(lib().frozen_awq_workspace_bytes(rows), x.device, workspace)
     _check(lib().frozen_awq_forward(_ptr(x), _dt(x), rows, C.byref(wc), _ptr(y),
                                     _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return y
+
+
+# ------------------------------------------------------------------ MXFP8 activations
+def mx8_quantize(x: torch.Tensor):
+    """OCP MXFP8 quantization of bf16 rows: (codes uint8 [rows, K], scales uint8 [rows, K/32])."""
+    rows, K = x.shape
+    q = torch.empty(rows, K, dtype=torch.uint8, device=x.device)
+    s = torch.empty(rows, K // 32, dtype=torch.uint8, device=x.device)
+    _check(lib().mx8_quantize(_ptr(x), _dt(x), rows, K, _ptr(q), _ptr(s), _stream(x.device)))
+    return q, s
+
+
+def _mx8_workspace(rows: int, K: int, device, workspace):
+    return _workspace(int(lib().mx8_workspace_bytes(rows, K)), device, workspace)
+
+
+def mx8_grouped_swiglu(route: RouteState, values: torch.Tensor, gate_up: Mxfp4Bank,
+                       clamp: float = 0.0, alpha: float = 1.0, up_offset: float = 0.0,
+                       gate_one_sided: bool = False, h: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Interleaved gate/up bank on the block-scaled MFMA with MXFP8 values -> h [A, I] bf16."""
+    gc = gate_up.c()
+    if h is None:
+        h = torch.empty(values.shape[0], gc.out_features // 2, dtype=values.dtype,
+                        device=values.device)
+    workspace = _mx8_workspace(values.shape[0], gc.in_features, values.device, workspace)
+    _check(lib().mx8_grouped_swiglu(C.byref(route.c), _ptr(values), _dt(values), C.byref(gc),
+                                    SwiGLU(clamp, alpha, up_offset, int(gate_one_sided)),
+                                    _ptr(h), _ptr(workspace), workspace.numel(),
+                                    _stream(values.device)))
+    return h
+
+
+def mx8_grouped_down(route: RouteState, h: torch.Tensor, down: Mxfp4Bank,
+                     y: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Plain bank on the block-scaled MFMA with MXFP8 h -> y [A, K] bf16."""
+    dc = down.c()
+    if y is None:
+        y = torch.empty(h.shape[0], dc.out_features, dtype=h.dtype, device=h.device)
+    workspace = _mx8_workspace(h.shape[0], dc.in_features, h.device, workspace)
+    _check(lib().mx8_grouped_down(C.byref(route.c), _ptr(h), _dt(h), C.byref(dc), _ptr(y),
+                                  _ptr(workspace), workspace.numel(), _stream(h.device)))
     return y
 
 

@@ -316,3 +316,30 @@ def test_unsorted_and_single_projection_validation(L):
     assert single(wsp=0) == moeq.EINVAL
     assert single(nbytes=need1 - 1) == moeq.EWORKSPACE
     assert single(wsp=FAKE + 8) == moeq.EWORKSPACE
+
+
+def test_mx8_validation(L):
+    """The block-scaled MFMA path takes MXFP4 banks and bf16 rows only."""
+    P = C.c_void_p(FAKE)
+    assert L.mx8_workspace_bytes(100, 2880) >= 100 * 2880 + 100 * 90
+    assert L.mx8_workspace_bytes(100, 48) == 0 and L.mx8_workspace_bytes(-1, 64) == 0
+    assert L.mx8_quantize(P, moeq.F32, 4, 64, P, P, None) == moeq.EUNSUPPORTED
+    assert L.mx8_quantize(P, moeq.BF16, 4, 48, P, P, None) == moeq.ESHAPE
+    assert L.mx8_quantize(P, moeq.BF16, 0, 64, P, P, None) == moeq.OK
+    assert L.mx8_quantize(None, moeq.BF16, 4, 64, P, P, None) == moeq.EINVAL
+    _, r = bind(L, 4, 8, 2)
+    _, r0 = bind(L, 0, 8, 2)
+    need = L.mx8_workspace_bytes(8, 64)
+    fn = moeq.SwiGLU(7.0, 1.0, 0.0, 0)
+    sw = lambda route, w, act=moeq.BF16, wsp=FAKE, nbytes=need: L.mx8_grouped_swiglu(
+        C.byref(route), P, act, C.byref(w), fn, P, C.c_void_p(wsp) if wsp else None, nbytes, None)
+    assert sw(r0, bank(K=64, R=128)) == moeq.OK
+    assert sw(r, awq()) == moeq.EUNSUPPORTED
+    assert sw(r, bank(K=64, R=128, inter=0)) == moeq.ESHAPE      # gate/up needs the interleave
+    assert sw(r, bank(K=64, R=96)) == moeq.EUNSUPPORTED          # bank rows not a multiple of 64
+    assert sw(r, bank(K=64, R=128), act=moeq.F32) == moeq.EUNSUPPORTED
+    assert sw(r, bank(K=64, R=128), wsp=0) == moeq.EINVAL
+    assert sw(r, bank(K=64, R=128), nbytes=need - 1) == moeq.EWORKSPACE
+    dn = lambda w: L.mx8_grouped_down(C.byref(r), P, moeq.BF16, C.byref(w), P, P, need, None)
+    assert dn(bank(K=64, R=64, inter=1)) == moeq.ESHAPE
+    assert dn(awq()) == moeq.EUNSUPPORTED
