@@ -635,7 +635,9 @@ size_t mx8_workspace_bytes(int32_t rows, int32_t K) {
     if (rows < 0 || K < 32 || K % 32 != 0) return 0;
     size_t n;
     if (!mul_ok((size_t)rows, (size_t)K, &n)) return 0;
-    return align256(n ? n : 1) + align256(n / 32 ? n / 32 : 1);
+    // codes, then scale rows padded to 16 bytes
+    const size_t sstride = ((size_t)K / 32 + 15) / 16 * 16;
+    return align256(n ? n : 1) + align256((size_t)(rows ? rows : 1) * sstride);
 }
 
 moeq_status mx8_quantize(const void *x, moeq_dtype act, int32_t rows, int32_t K, uint8_t *q,
@@ -647,8 +649,9 @@ moeq_status mx8_quantize(const void *x, moeq_dtype act, int32_t rows, int32_t K,
     if (!x || !q || !s) return fail(MOEQ_EINVAL, "NULL tensor pointer");
     if ((uintptr_t)x % 16 != 0 || (uintptr_t)q % 16 != 0)
         return fail(MOEQ_EINVAL, "rows must be 16-byte aligned");
-    return device_status(launch_mx8_quant(x, rows, K, q, s, static_cast<hipStream_t>(stream)),
-                         "MXFP8 quantization");
+    return device_status(
+        launch_mx8_quant(x, rows, K, q, s, K / 32, static_cast<hipStream_t>(stream)),
+        "MXFP8 quantization");
 }
 
 namespace {
@@ -666,6 +669,10 @@ moeq_status mx8_check(const moeq_route *route, const void *in, moeq_dtype act,
     if (act != MOEQ_BF16) return fail(MOEQ_EUNSUPPORTED, "MXFP8 activations come from bf16 rows");
     if (w->out_features % 64 != 0)
         return fail(MOEQ_EUNSUPPORTED, "bank rows %d are not a multiple of 64", w->out_features);
+    if (w->in_features > 4096)
+        return fail(MOEQ_EUNSUPPORTED, "in_features %d above 4096", w->in_features);
+    if ((uintptr_t)w->scales % 16 != 0 || (uintptr_t)w->qweight % 16 != 0)
+        return fail(MOEQ_EINVAL, "bank blocks and scales must be 16-byte aligned");
     const int A = route->T * route->top_k;
     if (A == 0) return MOEQ_OK;
     if (!in) return fail(MOEQ_EINVAL, "NULL tensor pointer");
@@ -682,11 +689,13 @@ moeq_status mx8_run(const moeq_route *route, const void *in, const moeq_experts 
     const int A = route->T * route->top_k, K = w->in_features;
     uint8_t *q = static_cast<uint8_t *>(workspace);
     uint8_t *qs = q + align256((size_t)A * K);
+    const int sstride = (K / 32 + 15) / 16 * 16;
     moeq_status st;
-    if ((st = device_status(launch_mx8_quant(in, A, K, q, qs, s), "MXFP8 quantization")) !=
-        MOEQ_OK)
+    if ((st = device_status(launch_mx8_quant(in, A, K, q, qs, sstride, s),
+                            "MXFP8 quantization")) != MOEQ_OK)
         return st;
-    return device_status(launch_mx8_gemm(q, qs, A, K, operand_of(w), route->expert_offsets,
+    return device_status(launch_mx8_gemm(q, qs, sstride, A, K, operand_of(w),
+                                         route->expert_offsets,
                                          route->tile_offsets, route->tile_expert, route->E,
                                          swiglu, swiglu ? w->out_features / 2 : w->out_features,
                                          fn.clamp, gate_lower(fn), fn.alpha, fn.up_offset, out,

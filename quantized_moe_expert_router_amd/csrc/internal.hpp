@@ -88,8 +88,8 @@ hipError_t launch_combine_backward(const void *y, int act, const float *weights,
 hipError_t launch_swiglu_vjp(void *G, void *U, const void *dh, int act, size_t n, float clamp,
                              float gate_lo, float alpha, float up_offset, hipStream_t s);
 hipError_t launch_mx8_quant(const void *x, int rows, int K, uint8_t *q, uint8_t *s,
-                            hipStream_t st);
-hipError_t launch_mx8_gemm(const uint8_t *q, const uint8_t *qs, int rows, int K,
+                            int sstride, hipStream_t st);
+hipError_t launch_mx8_gemm(const uint8_t *q, const uint8_t *qs, int sstride, int rows, int K,
                            const PackedOperand &w, const int32_t *offsets,
                            const int32_t *tile_offsets, const int32_t *tile_expert, int E,
                            bool swiglu, int Nout, float clamp, float gate_lo, float alpha,
