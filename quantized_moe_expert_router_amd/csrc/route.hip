@@ -53,23 +53,36 @@ __device__ __forceinline__ uint64_t row16_max(uint64_t k) {
 // maximum key, and its owner lane clears it.  Lane j < k receives slot j: its
 // expert and its weight, the softmax over the k selected scores evaluated in
 // double in slot order and rounded once to fp32.
+// The lane's logits and expert biases, loaded with clamped indices (no branch
+// around a load), so the lane waits once.
+template <int EPL>
+struct RouteRaw {
+    float v[EPL], b[EPL];
+};
+
 template <int LANES, int EPL>
-__device__ __forceinline__ void route_token(const float *__restrict__ logits,
-                                            const float *__restrict__ bias, int t, int E, int k,
-                                            int r, int group_base_lane, int *sel_out,
-                                            float *w_out) {
+__device__ __forceinline__ void route_load(const float *__restrict__ logits,
+                                           const float *__restrict__ bias, int t, int E, int r,
+                                           RouteRaw<EPL> &raw) {
     const float *row = logits + (size_t)t * E;
-    // all loads first (clamped index, no branch), so the lane waits once
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) raw.v[i] = row[min(r + LANES * i, E - 1)];
+    if (bias) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) raw.b[i] = bias[min(r + LANES * i, E - 1)];
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) raw.b[i] = 0.0f;  // unused: no add without a bias
+    }
+}
+
+template <int LANES, int EPL>
+__device__ __forceinline__ void route_select(const RouteRaw<EPL> &raw, bool has_bias, int E,
+                                             int k, int r, int group_base_lane, int *sel_out,
+                                             float *w_out) {
     float v[EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) v[i] = row[min(r + LANES * i, E - 1)];
-    if (bias) {
-        float b[EPL];
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) b[i] = bias[min(r + LANES * i, E - 1)];
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) v[i] = v[i] + b[i];  // one IEEE fp32 add
-    }
+    for (int i = 0; i < EPL; ++i) v[i] = has_bias ? raw.v[i] + raw.b[i] : raw.v[i];  // one fp32 add
     uint64_t key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
@@ -97,6 +110,16 @@ __device__ __forceinline__ void route_token(const float *__restrict__ logits,
     for (int j = 0; j < k; ++j) den += __shfl(ex, group_base_lane + j);  // slot order
     *sel_out = key_expert(mine);
     *w_out = (float)(ex / den);
+}
+
+template <int LANES, int EPL>
+__device__ __forceinline__ void route_token(const float *__restrict__ logits,
+                                            const float *__restrict__ bias, int t, int E, int k,
+                                            int r, int group_base_lane, int *sel_out,
+                                            float *w_out) {
+    RouteRaw<EPL> raw;
+    route_load<LANES, EPL>(logits, bias, t, E, r, raw);
+    route_select<LANES, EPL>(raw, bias != nullptr, E, k, r, group_base_lane, sel_out, w_out);
 }
 
 template <int LANES, int EPL>
@@ -144,7 +167,15 @@ hipError_t launch_router(const float *logits, const float *bias, int T, int E, i
 // expert histogram, exclusive scan, and the rank of token t among the tokens
 // of expert e as a popcount over a per-expert token bitmask -- then block 0
 // writes the routing outputs and every block copies its share of rows.
+//
+// The copy runs over source vectors: x is [T][vecs] 16-byte vectors, and
+// vector (t, i) goes to row slot_pos[t, j] of every slot j.  A thread's first
+// kPre vectors are loaded right behind the first routing pass's logits, so
+// their latency overlaps the routing, and stored once the positions are known
+// (not for E > 128, whose routing already fills the registers).
 constexpr int kSmallT = 256, kSmallA = 4096, kSmallE = 256, kSmallK = 16;
+constexpr int kPre = 2;  // source vectors per thread loaded during the routing (E <= 128)
+typedef uint32_t vec4u __attribute__((ext_vector_type(4)));  // kept in registers
 
 template <int EPL>
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(
@@ -156,7 +187,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
     int32_t *__restrict__ tile_offsets_g, int32_t *__restrict__ tile_expert_g) {
     __shared__ uint16_t sel_s[kSmallA];
     __shared__ float w_s[kSmallA];
-    __shared__ int32_t rsrc_s[kSmallA];
+    __shared__ int32_t pos_s[kSmallA];
     __shared__ int32_t hist_s[kSmallE];
     __shared__ int32_t off_s[kSmallE + 1];
     __shared__ unsigned long long mask_s[kSmallE][kSmallT / 64];
@@ -164,18 +195,39 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
     const int tid = threadIdx.x, A = T * k;
     const int MW = (T + 63) / 64;
 
-    // 1. routing: 64 rows of 16 lanes per pass
-    for (int t0 = 0; t0 < T; t0 += 64) {
-        const int t = t0 + (tid >> 4), r = tid & 15;
+    const int vecs = row_bytes / 16;
+    const long npairs = (long)T * vecs;  // source vectors
+    const long gtid = (long)blockIdx.x * blockDim.x + tid, gstride = (long)gridDim.x * blockDim.x;
+    const vec4u *__restrict__ xv = reinterpret_cast<const vec4u *>(x);
+    constexpr int PRE = EPL <= 8 ? kPre : 0;
+    vec4u pre[PRE > 0 ? PRE : 1];
+
+    // 1. routing: 64 rows of 16 lanes per pass (loads at a clamped token, so
+    //    no load sits in a branch); the first pass also issues the prefetch
+    auto route_finish = [&](int t, int r, const RouteRaw<EPL> &raw) {
         if (t < T) {
             int sel;
             float w;
-            route_token<16, EPL>(logits, bias, t, E, k, r, (tid & 63) & ~15, &sel, &w);
+            route_select<16, EPL>(raw, bias != nullptr, E, k, r, (tid & 63) & ~15, &sel, &w);
             if (r < k) {
                 sel_s[t * k + r] = (uint16_t)sel;
                 w_s[t * k + r] = w;
             }
         }
+    };
+    {
+        const int t = tid >> 4, r = tid & 15;
+        RouteRaw<EPL> raw;
+        route_load<16, EPL>(logits, bias, min(t, T - 1), E, r, raw);
+#pragma unroll
+        for (int u = 0; u < PRE; ++u) pre[u] = xv[min(gtid + u * gstride, npairs - 1)];
+        route_finish(t, r, raw);
+    }
+    for (int t0 = 64; t0 < T; t0 += 64) {
+        const int t = t0 + (tid >> 4), r = tid & 15;
+        RouteRaw<EPL> raw;
+        route_load<16, EPL>(logits, bias, min(t, T - 1), E, r, raw);
+        route_finish(t, r, raw);
     }
     for (int e = tid; e < E; e += blockDim.x) {
         hist_s[e] = 0;
@@ -233,7 +285,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
         int rank = __popcll(mask_s[e][t >> 6] & ((1ull << (t & 63)) - 1ull));
         for (int mw = 0; mw < (t >> 6); ++mw) rank += __popcll(mask_s[e][mw]);
         const int p = off_s[e] + rank;
-        rsrc_s[p] = t;
+        pos_s[a] = p;
         if (blockIdx.x == 0) {
             slot_pos_g[a] = p;
             row_src_g[p] = t;
@@ -245,40 +297,27 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
     if (blockIdx.x == 0)
         for (int e = tid; e <= E; e += blockDim.x) offsets[e] = off_s[e];
     __syncthreads();
-    // 5. row copies: the grid walks the flattened (row, 16-byte vector) space;
-    //    each thread issues its four loads before its four stores, so the copy
-    //    costs one memory round trip instead of one per row
-    const int vecs = row_bytes / 16;
-    const long total = (long)A * vecs, stride = (long)gridDim.x * blockDim.x * 4;
-    for (long base = (long)blockIdx.x * blockDim.x * 4 + tid; base < total; base += stride) {
-        const long step = blockDim.x;
-        if (base + 3 * step < total) {
-            const uint4 *src[4];
-            uint4 *dst[4];
+    // 5. row copies: each source vector is stored to the rows of the token's k
+    //    slots (for a fixed slot, consecutive threads write consecutive vectors)
+    vec4u *__restrict__ vv = reinterpret_cast<vec4u *>(values);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const long idx = base + u * step;
-                const int p = (int)(idx / vecs), i = (int)(idx % vecs);
-                src[u] = reinterpret_cast<const uint4 *>(x + (size_t)rsrc_s[p] * row_bytes) + i;
-                dst[u] = reinterpret_cast<uint4 *>(values + (size_t)p * row_bytes) + i;
-            }
-            const uint4 v0 = *src[0], v1 = *src[1], v2 = *src[2], v3 = *src[3];
-            *dst[0] = v0;
-            *dst[1] = v1;
-            *dst[2] = v2;
-            *dst[3] = v3;
-        } else {
-            for (long idx = base; idx < total; idx += step) {
-                const int p = (int)(idx / vecs), i = (int)(idx % vecs);
-                reinterpret_cast<uint4 *>(values + (size_t)p * row_bytes)[i] =
-                    reinterpret_cast<const uint4 *>(x + (size_t)rsrc_s[p] * row_bytes)[i];
-            }
+    for (int u = 0; u < PRE; ++u) {
+        const long pr = gtid + u * gstride;
+        if (pr < npairs) {
+            const int t = (int)(pr / vecs), i = (int)(pr - (long)t * vecs);
+            for (int j = 0; j < k; ++j) vv[(size_t)pos_s[t * k + j] * vecs + i] = pre[u];
         }
+    }
+    for (long pr = gtid + PRE * gstride; pr < npairs; pr += gstride) {
+        const vec4u v = xv[pr];
+        const int t = (int)(pr / vecs), i = (int)(pr - (long)t * vecs);
+        for (int j = 0; j < k; ++j) vv[(size_t)pos_s[t * k + j] * vecs + i] = v;
     }
 }
 
 bool small_dispatch_fits(int T, int E, int k, size_t row_bytes, const void *x, const void *values) {
-    return T <= kSmallT && T * k <= kSmallA && E <= kSmallE && k <= kSmallK && row_bytes % 16 == 0 &&
+    return T >= 1 && T <= kSmallT && T * k <= kSmallA && E <= kSmallE && k <= kSmallK &&
+           row_bytes >= 16 && row_bytes % 16 == 0 &&
            ((uintptr_t)x | (uintptr_t)values) % 16 == 0 && row_bytes < ((size_t)1 << 30);
 }
 
