@@ -33,7 +33,8 @@
  *  - All tensor arguments are device pointers to contiguous row-major memory
  *    owned by the caller.  The library allocates no device memory, frees
  *    nothing, and does not synchronise, except moe_dispatch_counts, which
- *    returns host values and therefore synchronises its stream.
+ *    returns host values, and awq_expert_forward / awq_expert_input_backward,
+ *    which validate their expert IDs on the host; these synchronise `stream`.
  *  - `stream` is a hipStream_t (NULL = the default stream).  All kernels of a
  *    call are enqueued on it; the call returns once they are enqueued.
  *  - Arguments are validated on the host before anything is enqueued.  On a
