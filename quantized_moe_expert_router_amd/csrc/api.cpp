@@ -283,6 +283,9 @@ moeq_status moe_dispatch(const void *x, moeq_dtype act, int32_t T, int32_t K,
     if ((st = device_status(launch_dispatch_index(selected, T, E, top_k, route, row_experts, s),
                             "dispatch index")) != MOEQ_OK)
         return st;
+    if (scatter_rows_fits(row_bytes, top_k, x, values))  // each source row read once
+        return device_status(launch_scatter_rows(x, row_bytes, T, top_k, route->slot_pos, values, s),
+                             "row scatter");
     return device_status(launch_copy_rows(x, row_bytes, T * top_k, route->row_src, values, s),
                          "row copy");
 }

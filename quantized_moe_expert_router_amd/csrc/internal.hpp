@@ -68,6 +68,9 @@ hipError_t launch_dispatch_small(const void *x, size_t row_bytes, const float *l
 hipError_t launch_dispatch_index(const uint32_t *selected, int T, int E, int k,
                                  const moeq_route *route, uint32_t *row_experts,
                                  hipStream_t s);
+bool scatter_rows_fits(size_t row_bytes, int k, const void *x, const void *values);
+hipError_t launch_scatter_rows(const void *x, size_t row_bytes, int T, int k,
+                               const int32_t *slot_pos, void *values, hipStream_t s);
 hipError_t launch_copy_rows(const void *x, size_t row_bytes, int A, const int32_t *row_src,
                             void *values, hipStream_t s);
 hipError_t launch_local_ids(const uint32_t *gid, int rows, int start, uint32_t *local,

@@ -575,6 +575,62 @@ hipError_t launch_copy_rows(const void *x, size_t row_bytes, int A, const int32_
     return hipGetLastError();
 }
 
+// Source-major COPY dispatch for large batches: x is [T][vecs] 16-byte
+// vectors, and vector (t, i) goes to row slot_pos[t, j] of each slot j.  A
+// block covers kScatterU * 256 consecutive source vectors; each thread loads
+// its kScatterU vectors at once (clamped, no branch around a load) while the
+// block stages the slot positions of its tokens in LDS, then stores every
+// vector k times (for a fixed slot, consecutive threads write consecutive
+// vectors).  Each source row is read once instead of once per slot.
+constexpr int kScatterU = 4;
+constexpr int kScatterMinVecs = 16;  // at most 65 tokens per block
+constexpr int kScatterTokens = (256 * kScatterU) / kScatterMinVecs + 1;
+
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const vec4u *__restrict__ x, int vecs,
+                                                           int T, int k,
+                                                           const int32_t *__restrict__ slot_pos,
+                                                           vec4u *__restrict__ values) {
+    __shared__ int32_t pos_s[kScatterTokens * kMaxTopK];
+    const long n = (long)T * vecs;
+    const long b0 = (long)blockIdx.x * (256 * kScatterU);
+    const long b1 = min(b0 + 256 * kScatterU, n);
+    const int t_lo = (int)(b0 / vecs), t_hi = (int)((b1 - 1) / vecs);
+    vec4u v[kScatterU];
+#pragma unroll
+    for (int u = 0; u < kScatterU; ++u)
+        v[u] = x[min(b0 + u * 256 + (long)threadIdx.x, n - 1)];
+    const int cnt = (t_hi - t_lo + 1) * k;
+    for (int i = threadIdx.x; i < cnt; i += 256) pos_s[i] = slot_pos[(size_t)t_lo * k + i];
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kScatterU; ++u) {
+        const long pr = b0 + u * 256 + (long)threadIdx.x;
+        if (pr < n) {
+            const int t = (int)(pr / vecs), i = (int)(pr - (long)t * vecs);
+            const int32_t *pt = pos_s + (t - t_lo) * k;
+            for (int j = 0; j < k; ++j) values[(size_t)pt[j] * vecs + i] = v[u];
+        }
+    }
+}
+
+bool scatter_rows_fits(size_t row_bytes, int k, const void *x, const void *values) {
+    return row_bytes % 16 == 0 && row_bytes / 16 >= (size_t)kScatterMinVecs &&
+           row_bytes / 16 < ((size_t)1 << 30) && k >= 1 && k <= kMaxTopK &&
+           ((uintptr_t)x | (uintptr_t)values) % 16 == 0;
+}
+
+hipError_t launch_scatter_rows(const void *x, size_t row_bytes, int T, int k,
+                               const int32_t *slot_pos, void *values, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const int vecs = (int)(row_bytes / 16);
+    const long n = (long)T * vecs;
+    const long blocks = (n + 256 * kScatterU - 1) / (256 * kScatterU);
+    if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (const vec4u *)x, vecs, T, k, slot_pos, (vec4u *)values);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ combine
 // One block per token.  The k sorted positions are ranked so that slot a of
 // the shared list is the a-th smallest position, i.e. the a-th smallest expert
