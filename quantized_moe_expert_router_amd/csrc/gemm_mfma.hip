@@ -64,9 +64,10 @@ struct StreamArgs {
 // columns = 128 output columns).  Its waves are NSETS x SPW x KSPLIT: wave
 // (set, strip, q) streams one strip of one cube (gate or up, or the single
 // down cube) over K slice q.  The waves of a block advance in lockstep (a
-// barrier per 128-row group), so the CU reads each row block of its part as
-// one contiguous piece -- one wave per strip would leave every row split over
-// several XCDs and halve the achieved bandwidth.
+// barrier per 128 rows, and per 32-row step for the pipelined gate/up
+// variant), so the CU reads each row block of its part as one contiguous
+// piece -- one wave per strip would leave every row split over several XCDs
+// and halve the achieved bandwidth.
 //
 // Per wave and 32-row step: eight buffer loads of one word per lane (row
 // offsets are scalar), nibble planes, codes through the fp8 converter, one fma
@@ -227,6 +228,10 @@ void awq_stream_kernel(StreamArgs a) {
                                            W, N, graw);
                         __builtin_amdgcn_sched_barrier(0);
                     }
+                    // gate/up: lockstep per 32-row step, so the CU keeps reading one
+                    // row block at a time (once per 128-row group was 4% slower;
+                    // the down projection is faster with one per group)
+                    if (NSETS == 2 && t > 0) lockstep_barrier();
                     step(wd[d], av[d], [&] { issue_words(d, kn); });
                     issue_rows(d, kn);
                 }
