@@ -47,6 +47,41 @@ __device__ __forceinline__ uint64_t row16_max(uint64_t k) {
     return k;
 }
 
+// Sorts a lane's keys in descending order (bitonic network, N a power of two).
+template <int N>
+__device__ __forceinline__ void sort_keys_desc(uint64_t (&a)[N]) {
+#pragma unroll
+    for (int size = 2; size <= N; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int l = i ^ stride;
+                if (l > i) {
+                    const bool desc = (i & size) == 0;  // direction of this bitonic run
+                    const uint64_t x = a[i], y = a[l];
+                    const bool sw = desc ? x < y : x > y;
+                    a[i] = sw ? y : x;
+                    a[l] = sw ? x : y;
+                }
+            }
+}
+
+// Per-lane select by a wave lane mask, as one v_cndmask per 32-bit half.  The
+// pop below is a chain of these; written as C selects, the compiler rewrote
+// the chain into a compare-heavy state machine of twice the length.
+__device__ __forceinline__ uint64_t select_by_mask(uint64_t lanes, uint64_t if_set,
+                                                   uint64_t if_clear) {
+    uint32_t lo, hi;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3"
+        : "=v"(lo)
+        : "v"((uint32_t)if_clear), "v"((uint32_t)if_set), "s"(lanes));
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3"
+        : "=v"(hi)
+        : "v"((uint32_t)(if_clear >> 32)), "v"((uint32_t)(if_set >> 32)), "s"(lanes));
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // Routes token t with the LANES lanes of the calling group (16: a DPP row; 64:
 // the whole wave, rows joined by two cross-row shuffles).  Lane r holds the
 // scores of experts r, r+LANES, ...; each of the k rounds takes the group-wide
@@ -76,7 +111,7 @@ __device__ __forceinline__ void route_load(const float *__restrict__ logits,
     }
 }
 
-template <int LANES, int EPL>
+template <int LANES, int EPL, bool SORTED = (EPL <= 16)>
 __device__ __forceinline__ void route_select(const RouteRaw<EPL> &raw, bool has_bias, int E,
                                              int k, int r, int group_base_lane, int *sel_out,
                                              float *w_out) {
@@ -90,18 +125,36 @@ __device__ __forceinline__ void route_select(const RouteRaw<EPL> &raw, bool has_
         key[i] = e < E ? sel_key(v[i], e) : 0;
     }
     uint64_t mine = 0;
-    for (int j = 0; j < k; ++j) {
-        uint64_t best = 0;
+    if constexpr (SORTED) {
+        // sorted lane lists: each round compares the heads only, and the lane
+        // that owns the maximum pops it (keys are unique, so exactly one lane)
+        sort_keys_desc<EPL>(key);
+        for (int j = 0; j < k; ++j) {
+            uint64_t best = row16_max(key[0]);
+            if (LANES == 64) {
+                best = umax64(best, __shfl_xor(best, 16));
+                best = umax64(best, __shfl_xor(best, 32));
+            }
+            const uint64_t win = __builtin_amdgcn_ballot_w64(key[0] == best);
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) best = umax64(best, key[i]);
-        best = row16_max(best);
-        if (LANES == 64) {
-            best = umax64(best, __shfl_xor(best, 16));
-            best = umax64(best, __shfl_xor(best, 32));
+            for (int i = 0; i + 1 < EPL; ++i) key[i] = select_by_mask(win, key[i + 1], key[i]);
+            key[EPL - 1] = select_by_mask(win, 0, key[EPL - 1]);
+            mine = r == j ? best : mine;
         }
+    } else {
+        for (int j = 0; j < k; ++j) {
+            uint64_t best = 0;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) key[i] = key[i] == best ? 0 : key[i];  // taken
-        mine = r == j ? best : mine;
+            for (int i = 0; i < EPL; ++i) best = umax64(best, key[i]);
+            best = row16_max(best);
+            if (LANES == 64) {
+                best = umax64(best, __shfl_xor(best, 16));
+                best = umax64(best, __shfl_xor(best, 32));
+            }
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) key[i] = key[i] == best ? 0 : key[i];  // taken
+            mine = r == j ? best : mine;
+        }
     }
     const float my_score = key_score(mine);
     const double m = (double)__shfl(my_score, group_base_lane);
@@ -208,7 +261,10 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
         if (t < T) {
             int sel;
             float w;
-            route_select<16, EPL>(raw, bias != nullptr, E, k, r, (tid & 63) & ~15, &sel, &w);
+            // 16 keys per lane (E > 128) stay unsorted: the sort would spill at
+            // 1024 threads per block
+            route_select<16, EPL, (EPL <= 8)>(raw, bias != nullptr, E, k, r, (tid & 63) & ~15,
+                                             &sel, &w);
             if (r < k) {
                 sel_s[t * k + r] = (uint16_t)sel;
                 w_s[t * k + r] = w;
