@@ -15,7 +15,7 @@ import oracle
 from gpu_util import DEV, TOL, f64, row_rel_err, run_path
 from quantized_moe_expert_router_amd import device_inputs as di
 from quantized_moe_expert_router_amd import moeq
-from quantized_moe_expert_router_amd.synth import CONFIGS, make_inputs
+from quantized_moe_expert_router_amd.synth import CONFIGS, make_inputs, to_storage
 
 pytestmark = pytest.mark.gpu
 
@@ -82,6 +82,27 @@ def test_dispatch_many_experts_many_blocks(T, E, k):
     np.testing.assert_array_equal(r.slot_pos.cpu().numpy(), pos)
     np.testing.assert_array_equal(disp["row_experts"].cpu().numpy().view(np.uint32), rex)
     np.testing.assert_array_equal(disp["values"].cpu().numpy(), oracle.copy_rows(x, src))
+
+
+@pytest.mark.parametrize("T,E,k,K,adt", [
+    (301, 64, 32, 128, "bf16"),   # 256-byte rows: 16 vectors, blocks aligned to 64 tokens, k at the limit
+    (300, 128, 8, 136, "bf16"),   # 272-byte rows: blocks straddle tokens
+    (300, 128, 4, 120, "bf16"),   # 240-byte rows: below the scatter's minimum, row-copy kernel
+    (257, 32, 6, 64, "f32"),      # 256-byte fp32 rows
+])
+def test_dispatch_row_scatter_edges(T, E, k, K, adt):
+    """Large-batch COPY at the edges of the source-major scatter (rows of at least
+    16 vectors; its LDS holds the slot positions of at most 65 tokens)."""
+    rng = np.random.default_rng(T + 3 * E + k + K)
+    logits = rng.normal(0, 1, (T, E)).astype(np.float32)
+    x = to_storage(rng.normal(0, 1, (T, K)), adt)
+    print(f"[dispatch-scatter] T={T} E={E} k={k} K={K} {adt}", flush=True)
+    disp = moeq.moe_dispatch(di.tensor(x, adt, DEV), torch.from_numpy(logits).to(DEV), None, k)
+    torch.cuda.synchronize()
+    sel, _ = oracle.route(logits, None, k)
+    _, src, pos, _ = oracle.dispatch_index(sel, E)
+    np.testing.assert_array_equal(disp["route"].slot_pos.cpu().numpy(), pos)
+    np.testing.assert_array_equal(di.to_host(disp["values"], adt), oracle.copy_rows(x, src))
 
 
 @pytest.mark.parametrize("T,E,k", [(300, 128, 8), (77, 16, 4), (64, 512, 10), (5, 32, 32)])
