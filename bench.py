@@ -233,7 +233,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path "
-              "shards by tokens or by expert ranges, but measures a single GPU)",
+              "would shard by tokens or by expert ranges across GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
