@@ -29,8 +29,10 @@
 // cube * 256 + sl * 32 + wc (gate/up) or sl * 64 + wc (one cube): a 16-column
 // MFMA tile is 16 consecutive word columns of one nibble slot.
 //
-// Blocks: m-tiles split into eight contiguous ranges, one per XCD (block b
-// runs on XCD b % 8).
+// Blocks: m-tiles dealt round-robin to the eight XCDs (block b runs on XCD
+// b % 8), so a heavy expert's m-tiles spread over all of them.  Contiguous
+// ranges per XCD (an expert's m-tiles sharing one L2) were 5% slower on the
+// many-expert workload, where a few experts hold most rows.
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
@@ -84,12 +86,12 @@ void awq_ws_kernel(WsArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 As[2][kRows][32];     // 16 KiB
     __shared__ __attribute__((aligned(16))) __bf16 Bs[2][kBCols][32];    // 64 KiB
 
-    // ---- block -> (m-tile, column block); contiguous m-tile ranges per XCD
+    // ---- block -> (m-tile, column block); m-tile mt runs on XCD mt % 8
     const int mtiles = a.tile_offsets[a.E];
     const int per_xcd = (mtiles + 7) / 8;
     const int x = blockIdx.x % 8, idx = blockIdx.x / 8;
     const int local = idx / a.nblk, nb = idx % a.nblk;
-    const int mt = x * per_xcd + local;
+    const int mt = local * 8 + x;
     if (local >= per_xcd || mt >= mtiles) return;
     const int e = a.tile_expert[mt];
     const int m0 = a.offsets[e] + (mt - a.tile_offsets[e]) * kRows;
