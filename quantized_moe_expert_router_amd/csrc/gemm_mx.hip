@@ -22,8 +22,9 @@
 // (n0 + c) / 2; a DPP swap of adjacent lanes pairs them for SwiGLU.
 //
 // Blocks: one m-tile (128 rows of one expert) x 8 waves x 48 bank rows.  The
-// m-tiles are split into eight contiguous ranges, one per XCD (block b runs
-// on XCD b % 8), so the column blocks of an m-tile share its rows in L2.
+// m-tiles are dealt round-robin to the eight XCDs (block b runs on XCD b % 8;
+// contiguous ranges per XCD were 0.6% slower); the column blocks of an m-tile
+// run on one XCD and share its rows in L2.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -77,12 +78,12 @@ __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mx_wave_kernel(MxArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 As[2][kRows][kArow];  // 64 KB
 
-    // ---- block -> (m-tile, column block); contiguous m-tile ranges per XCD
+    // ---- block -> (m-tile, column block); m-tile mt runs on XCD mt % 8
     const int mtiles = a.tile_offsets[a.E];
     const int per_xcd = (mtiles + 7) / 8;
     const int x = blockIdx.x % 8, idx = blockIdx.x / 8;
     const int local = idx / a.nblk, nb = idx % a.nblk;
-    const int mt = x * per_xcd + local;
+    const int mt = local * 8 + x;  // m-tiles dealt round-robin to the XCDs
     if (local >= per_xcd || mt >= mtiles) return;
     const int e = a.tile_expert[mt];
     const int m0 = a.offsets[e] + (mt - a.tile_offsets[e]) * kRows;

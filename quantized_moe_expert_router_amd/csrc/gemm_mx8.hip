@@ -137,12 +137,12 @@ void mx8_gemm_kernel(Mx8Args a) {
     static_assert(kPer == 4, "stage layout");
     __shared__ __attribute__((aligned(16))) Mx8Lds<CG> lds;
 
-    // m-tiles in contiguous ranges per XCD (block b runs on XCD b % 8)
+    // m-tiles dealt round-robin to the XCDs (block b runs on XCD b % 8)
     const int mtiles = a.tile_offsets[a.E];
     const int per_xcd = (mtiles + 7) / 8;
     const int x = blockIdx.x % 8, idx = blockIdx.x / 8;
     const int local = idx / a.nblk, nb = idx % a.nblk;
-    const int mt = x * per_xcd + local;
+    const int mt = local * 8 + x;  // m-tiles dealt round-robin to the XCDs
     if (local >= per_xcd || mt >= mtiles) return;
     const int e = a.tile_expert[mt];
     const int m0 = a.offsets[e] + (mt - a.tile_offsets[e]) * kRows;
