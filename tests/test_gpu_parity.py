@@ -84,6 +84,36 @@ def test_dispatch_many_experts_many_blocks(T, E, k):
     np.testing.assert_array_equal(disp["values"].cpu().numpy(), oracle.copy_rows(x, src))
 
 
+@pytest.mark.parametrize("T,E,k", [
+    (50, 200, 6),      # fused small dispatch, 16 keys per lane (unsorted rounds)
+    (256, 256, 16),    # the fused kernel's largest shape: T = 256, A = 4096, E = 256, k = 16
+    (300, 200, 8),     # large batch: router with 16 sorted keys per lane on 16 lanes
+    (300, 256, 16),
+])
+def test_dispatch_over_128_experts(T, E, k):
+    """Routing, order and COPY bit-exact for 128 < E <= 256, where a 16-lane group
+    holds 16 keys per lane; a bias on a few experts creates score ties across
+    lanes and long per-lane runs of winners."""
+    rng = np.random.default_rng(T * 3 + E + k)
+    logits = np.round(rng.normal(0, 1, (T, E)) * 4).astype(np.float32) / 4   # many ties
+    bias = np.zeros(E, np.float32)
+    bias[rng.choice(E, 5, replace=False)] = 1.5
+    x = rng.normal(0, 1, (T, 64)).astype(np.float32)
+    print(f"[dispatch-E] T={T} E={E} k={k}", flush=True)
+    disp = moeq.moe_dispatch(torch.from_numpy(x).to(DEV), torch.from_numpy(logits).to(DEV),
+                             torch.from_numpy(bias).to(DEV), k)
+    torch.cuda.synchronize()
+    sel, w = oracle.route(logits, bias, k)
+    off, src, pos, rex = oracle.dispatch_index(sel, E)
+    r = disp["route"]
+    np.testing.assert_array_equal(disp["selected"].cpu().numpy().view(np.uint32), sel)
+    np.testing.assert_allclose(disp["weights"].cpu().numpy(), w, rtol=2.0 ** -23, atol=0)
+    np.testing.assert_array_equal(r.expert_offsets.cpu().numpy(), off)
+    np.testing.assert_array_equal(r.slot_pos.cpu().numpy(), pos)
+    np.testing.assert_array_equal(disp["row_experts"].cpu().numpy().view(np.uint32), rex)
+    np.testing.assert_array_equal(disp["values"].cpu().numpy(), oracle.copy_rows(x, src))
+
+
 @pytest.mark.parametrize("T,E,k,K,adt", [
     (301, 64, 32, 128, "bf16"),   # 256-byte rows: 16 vectors, blocks aligned to 64 tokens, k at the limit
     (300, 128, 8, 136, "bf16"),   # 272-byte rows: blocks straddle tokens
