@@ -47,6 +47,7 @@ struct StreamArgs {
     int parts;                // column parts per expert (blocks per expert)
     int E;                    // experts
     int xcd_pairs;            // 1: the parts of an expert share an XCD (see kernel)
+    int vec_out;              // 1: out is 16-byte aligned (one store per row of 8 columns)
     const uint32_t *qw[2];
     const uint32_t *qz[2];
     const void *sc[2];
@@ -309,26 +310,32 @@ void awq_stream_kernel(StreamArgs a) {
             __syncthreads();
         }
         if (q == 0 && set == 0) {
+            float b0[8], b1[8];  // by slot
 #pragma unroll
             for (int sl = 0; sl < 8; ++sl) {
                 const int col = 8 * j + kSlotCol[sl];
-                float b0 = 0.f, b1 = 0.f;
-                if (a.bias[0]) b0 = load_f<SD>(a.bias[0], (size_t)e * N + col);
-                if (NSETS == 2 && a.bias[1]) b1 = load_f<SD>(a.bias[1], (size_t)e * N + col);
+                b0[sl] = a.bias[0] ? load_f<SD>(a.bias[0], (size_t)e * N + col) : 0.f;
+                b1[sl] = (NSETS == 2 && a.bias[1]) ? load_f<SD>(a.bias[1], (size_t)e * N + col)
+                                                   : 0.f;
+            }
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    f32x4 up4 = f32x4{0.f, 0.f, 0.f, 0.f};
-                    if (NSETS == 2) up4 = red[strip][sl * RT + rt][lane];
+            for (int rt = 0; rt < RT; ++rt) {
+                f32x4 up4[8];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = m0 + rt * 16 + grp * 4 + i;
-                        if (row >= r1) continue;
-                        float v;
+                for (int sl = 0; sl < 8; ++sl)
+                    up4[sl] = NSETS == 2 ? red[strip][sl * RT + rt][lane] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = m0 + rt * 16 + grp * 4 + i;
+                    if (row >= r1) continue;
+                    float v[8];  // by slot
+#pragma unroll
+                    for (int sl = 0; sl < 8; ++sl) {
                         if (NSETS == 2) {
-                            const float gv = round_to<MOEQ_BF16>(acc[sl][rt][i] + b0);
-                            const float uv = round_to<MOEQ_BF16>(up4[i] + b1);
+                            const float gv = round_to<MOEQ_BF16>(acc[sl][rt][i] + b0[sl]);
+                            const float uv = round_to<MOEQ_BF16>(up4[sl][i] + b1[sl]);
                             if constexpr (BWD) {  // backward: dG, dU at the rounded G, U
-                                const size_t at = (size_t)row * N + col;
+                                const size_t at = (size_t)row * N + 8 * j + kSlotCol[sl];
                                 float dg, du;
                                 swiglu_vjp_f(gv, uv, (float)a.dh[at], a.clamp, a.gate_lo, a.alpha,
                                              a.up_offset, &dg, &du);
@@ -336,11 +343,25 @@ void awq_stream_kernel(StreamArgs a) {
                                 a.out2[at] = (__bf16)du;
                                 continue;
                             }
-                            v = swiglu_f(gv, uv, a.clamp, a.gate_lo, a.alpha, a.up_offset);
+                            v[sl] = swiglu_f(gv, uv, a.clamp, a.gate_lo, a.alpha, a.up_offset);
                         } else {
-                            v = acc[sl][rt][i] + b0;
+                            v[sl] = acc[sl][rt][i] + b0[sl];
                         }
-                        a.out[(size_t)row * N + col] = (__bf16)v;
+                    }
+                    if constexpr (!BWD) {
+                        // the lane's 8 columns 8 j .. 8 j + 7 are slots 0 2 4 6 1 3 5 7
+                        __bf16 *o = a.out + (size_t)row * N + 8 * j;
+                        if (a.vec_out) {
+                            u32x4 pk;
+                            pk[0] = pack_bf16(v[0], v[2]);
+                            pk[1] = pack_bf16(v[4], v[6]);
+                            pk[2] = pack_bf16(v[1], v[3]);
+                            pk[3] = pack_bf16(v[5], v[7]);
+                            *reinterpret_cast<u32x4 *>(o) = pk;
+                        } else {
+#pragma unroll
+                            for (int sl = 0; sl < 8; ++sl) o[kSlotCol[sl]] = (__bf16)v[sl];
+                        }
                     }
                 }
             }
@@ -454,6 +475,7 @@ hipError_t run_stream(const ProjProblem &p, hipStream_t s) {
     }
     a.parts = strips / spw;
     a.E = p.E;
+    a.vec_out = ((uintptr_t)p.out % 16) == 0;
     a.xcd_pairs = 1;
     if (const char *v = getenv("MOEQ_STREAM_XCD")) a.xcd_pairs = atoi(v) != 0;
 #define MOEQ_SPW(X) \

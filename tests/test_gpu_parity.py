@@ -84,6 +84,27 @@ def test_dispatch_many_experts_many_blocks(T, E, k):
     np.testing.assert_array_equal(disp["values"].cpu().numpy(), oracle.copy_rows(x, src))
 
 
+def test_stream_epilogue_unaligned_outputs():
+    """Outputs at a 2-byte offset take the stream kernel's per-column stores; they
+    must equal the one-store-per-row results of 16-byte aligned outputs bit for bit."""
+    p = make_inputs(CONFIGS["decode"])
+    print(f"[stream epilogue] T={p['T']} unaligned h and y", flush=True)
+    d = di.upload(p, DEV)
+    disp = moeq.moe_dispatch(d["x"], d["logits"], d["router_bias"], p["k"])
+    r, A = disp["route"], p["T"] * p["k"]
+    args = (p["clamp"], p["alpha"], p["up_offset"])
+    h_al = moeq.awq_grouped_swiglu(r, disp["values"], d["gate"], d["up_arg"], *args)
+    h_un = torch.empty(A * p["I"] + 1, dtype=torch.bfloat16, device=DEV)[1:].view(A, p["I"])
+    moeq.awq_grouped_swiglu(r, disp["values"], d["gate"], d["up_arg"], *args, h=h_un)
+    y_al = moeq.awq_grouped_down(r, h_al, d["down"])
+    y_un = torch.empty(A * p["H"] + 1, dtype=torch.bfloat16, device=DEV)[1:].view(A, p["H"])
+    moeq.awq_grouped_down(r, h_al, d["down"], y=y_un)
+    torch.cuda.synchronize()
+    assert h_un.data_ptr() % 16 != 0 and y_un.data_ptr() % 16 != 0
+    assert torch.equal(h_al, h_un)
+    assert torch.equal(y_al, y_un)
+
+
 @pytest.mark.parametrize("T,E,k", [
     (50, 200, 6),      # fused small dispatch, 16 keys per lane (unsorted rounds)
     (256, 256, 16),    # the fused kernel's largest shape: T = 256, A = 4096, E = 256, k = 16
