@@ -47,7 +47,7 @@ struct StreamArgs {
     int parts;                // column parts per expert (blocks per expert)
     int E;                    // experts
     int xcd_pairs;            // 1: the parts of an expert share an XCD (see kernel)
-    int vec_out;              // 1: out is 16-byte aligned (one store per row of 8 columns)
+    int vec_out;              // 1: out (and out2, dh) 16-byte aligned: one vector per row of 8 columns
     const uint32_t *qw[2];
     const uint32_t *qz[2];
     const void *sc[2];
@@ -328,29 +328,66 @@ void awq_stream_kernel(StreamArgs a) {
                 for (int i = 0; i < 4; ++i) {
                     const int row = m0 + rt * 16 + grp * 4 + i;
                     if (row >= r1) continue;
+                    const size_t base = (size_t)row * N + 8 * j;
+                    if constexpr (BWD) {
+                        // backward: dG, dU at the rounded G, U; dh read, dG and dU
+                        // written as one 16-byte vector per row when aligned
+                        float dv[8];  // by slot
+                        if (a.vec_out) {
+                            const u32x4 w = *reinterpret_cast<const u32x4 *>(a.dh + base);
+#pragma unroll
+                            for (int sl = 0; sl < 8; ++sl) {
+                                const int c = kSlotCol[sl];
+                                const uint32_t pair = w[c >> 1];
+                                dv[sl] = __uint_as_float((c & 1) ? (pair & 0xFFFF0000u) : (pair << 16));
+                            }
+                        } else {
+#pragma unroll
+                            for (int sl = 0; sl < 8; ++sl) dv[sl] = (float)a.dh[base + kSlotCol[sl]];
+                        }
+                        float dg[8], du[8];
+#pragma unroll
+                        for (int sl = 0; sl < 8; ++sl) {
+                            const float gv = round_to<MOEQ_BF16>(acc[sl][rt][i] + b0[sl]);
+                            const float uv = round_to<MOEQ_BF16>(up4[sl][i] + b1[sl]);
+                            swiglu_vjp_f(gv, uv, dv[sl], a.clamp, a.gate_lo, a.alpha, a.up_offset,
+                                         &dg[sl], &du[sl]);
+                        }
+                        if (a.vec_out) {
+                            u32x4 pg, pu;
+                            pg[0] = pack_bf16(dg[0], dg[2]);
+                            pg[1] = pack_bf16(dg[4], dg[6]);
+                            pg[2] = pack_bf16(dg[1], dg[3]);
+                            pg[3] = pack_bf16(dg[5], dg[7]);
+                            pu[0] = pack_bf16(du[0], du[2]);
+                            pu[1] = pack_bf16(du[4], du[6]);
+                            pu[2] = pack_bf16(du[1], du[3]);
+                            pu[3] = pack_bf16(du[5], du[7]);
+                            *reinterpret_cast<u32x4 *>(a.out + base) = pg;
+                            *reinterpret_cast<u32x4 *>(a.out2 + base) = pu;
+                        } else {
+#pragma unroll
+                            for (int sl = 0; sl < 8; ++sl) {
+                                a.out[base + kSlotCol[sl]] = (__bf16)dg[sl];
+                                a.out2[base + kSlotCol[sl]] = (__bf16)du[sl];
+                            }
+                        }
+                        continue;
+                    }
                     float v[8];  // by slot
 #pragma unroll
                     for (int sl = 0; sl < 8; ++sl) {
                         if (NSETS == 2) {
                             const float gv = round_to<MOEQ_BF16>(acc[sl][rt][i] + b0[sl]);
                             const float uv = round_to<MOEQ_BF16>(up4[sl][i] + b1[sl]);
-                            if constexpr (BWD) {  // backward: dG, dU at the rounded G, U
-                                const size_t at = (size_t)row * N + 8 * j + kSlotCol[sl];
-                                float dg, du;
-                                swiglu_vjp_f(gv, uv, (float)a.dh[at], a.clamp, a.gate_lo, a.alpha,
-                                             a.up_offset, &dg, &du);
-                                a.out[at] = (__bf16)dg;
-                                a.out2[at] = (__bf16)du;
-                                continue;
-                            }
                             v[sl] = swiglu_f(gv, uv, a.clamp, a.gate_lo, a.alpha, a.up_offset);
                         } else {
                             v[sl] = acc[sl][rt][i] + b0[sl];
                         }
                     }
-                    if constexpr (!BWD) {
+                    {
                         // the lane's 8 columns 8 j .. 8 j + 7 are slots 0 2 4 6 1 3 5 7
-                        __bf16 *o = a.out + (size_t)row * N + 8 * j;
+                        __bf16 *o = a.out + base;
                         if (a.vec_out) {
                             u32x4 pk;
                             pk[0] = pack_bf16(v[0], v[2]);
@@ -475,7 +512,7 @@ hipError_t run_stream(const ProjProblem &p, hipStream_t s) {
     }
     a.parts = strips / spw;
     a.E = p.E;
-    a.vec_out = ((uintptr_t)p.out % 16) == 0;
+    a.vec_out = (((uintptr_t)p.out | (uintptr_t)p.out2 | (uintptr_t)p.in2) % 16) == 0;
     a.xcd_pairs = 1;
     if (const char *v = getenv("MOEQ_STREAM_XCD")) a.xcd_pairs = atoi(v) != 0;
 #define MOEQ_SPW(X) \
