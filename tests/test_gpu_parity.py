@@ -84,6 +84,28 @@ def test_dispatch_many_experts_many_blocks(T, E, k):
     np.testing.assert_array_equal(disp["values"].cpu().numpy(), oracle.copy_rows(x, src))
 
 
+@pytest.mark.parametrize("k,adt", [(9, "bf16"), (17, "bf16"), (32, "bf16"), (32, "f32")])
+def test_combine_many_slots(k, adt):
+    """Combine and COPY VJP for top_k above 8 (the 16- and 32-slot instances, with
+    padded slots): both bit-exact against the oracle's ascending-position fp32
+    chains on the same y, weights and gradients."""
+    T, E, K = 100, 64, 264                      # K = 264: a vector column tail
+    rng = np.random.default_rng(k * 13 + len(adt))
+    logits = rng.normal(0, 1, (T, E)).astype(np.float32)
+    x = to_storage(rng.normal(0, 1, (T, K)), adt)
+    print(f"[combine] T={T} E={E} k={k} K={K} {adt}", flush=True)
+    disp = moeq.moe_dispatch(di.tensor(x, adt, DEV), torch.from_numpy(logits).to(DEV), None, k)
+    A = T * k
+    y = to_storage(rng.normal(0, 1, (A, K)), adt)
+    out = moeq.moe_combine(disp["route"], di.tensor(y, adt, DEV), disp["weights"])
+    gx = moeq.moe_dispatch_backward(disp["route"], di.tensor(y, adt, DEV))
+    torch.cuda.synchronize()
+    pos = disp["route"].slot_pos.cpu().numpy().reshape(T, k)
+    w = disp["weights"].cpu().numpy()
+    np.testing.assert_array_equal(di.to_host(out, adt), oracle.combine(y, adt, w, pos))
+    np.testing.assert_array_equal(di.to_host(gx, adt), oracle.dispatch_backward(y, adt, pos))
+
+
 def test_stream_epilogue_unaligned_outputs():
     """Outputs at a 2-byte offset take the stream kernel's per-column stores; they
     must equal the one-store-per-row results of 16-byte aligned outputs bit for bit."""
