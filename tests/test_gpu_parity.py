@@ -86,9 +86,10 @@ def test_dispatch_many_experts_many_blocks(T, E, k):
 
 @pytest.mark.parametrize("k,adt", [(9, "bf16"), (17, "bf16"), (32, "bf16"), (32, "f32")])
 def test_combine_many_slots(k, adt):
-    """Combine and COPY VJP for top_k above 8 (the 16- and 32-slot instances, with
-    padded slots): both bit-exact against the oracle's ascending-position fp32
-    chains on the same y, weights and gradients."""
+    """Combine, COPY VJP and combine VJP for top_k above 8 (the 16- and 32-slot
+    instances, with padded slots) against the oracle on the same y, weights and
+    gradients: the fp32 chains bit-exact, the weight derivatives within the bound
+    of an fp64 sum rounded once."""
     T, E, K = 100, 64, 264                      # K = 264: a vector column tail
     rng = np.random.default_rng(k * 13 + len(adt))
     logits = rng.normal(0, 1, (T, E)).astype(np.float32)
@@ -104,6 +105,17 @@ def test_combine_many_slots(k, adt):
     w = disp["weights"].cpu().numpy()
     np.testing.assert_array_equal(di.to_host(out, adt), oracle.combine(y, adt, w, pos))
     np.testing.assert_array_equal(di.to_host(gx, adt), oracle.dispatch_backward(y, adt, pos))
+    # combine VJP: dy bit-exact; dweights within the fp64-sum-then-round bound
+    gout = to_storage(rng.normal(0, 1, (T, K)), adt)
+    gy, gw = moeq.moe_combine_backward(disp["route"], di.tensor(y, adt, DEV), disp["weights"],
+                                       di.tensor(gout, adt, DEV))
+    torch.cuda.synchronize()
+    ry, rw = oracle.combine_backward(y, adt, w, pos, gout)
+    np.testing.assert_array_equal(di.to_host(gy, adt), ry)
+    yf, gf = np.abs(f64(y, adt)), np.abs(f64(gout, adt))
+    absdot = np.stack([np.sum(gf * yf[pos[:, j]], axis=1) for j in range(k)], axis=1)
+    err = np.abs(gw.cpu().numpy().astype(np.float64) - rw.astype(np.float64))
+    assert np.all(err <= 2.0 ** -22 * np.abs(rw) + 2.0 ** -38 * absdot), float(err.max())
 
 
 def test_stream_epilogue_unaligned_outputs():
