@@ -24,11 +24,11 @@ pytestmark = pytest.mark.gpu
 class Step:
     """Fixed buffers for one configuration and the calls of one step."""
 
-    def __init__(self, p, d, backward):
+    def __init__(self, p, d, backward, mx8=False):
         T, k, E, H, I = p["T"], p["k"], p["E"], p["H"], p["I"]
         A = T * k
         adt = d["x"].dtype
-        self.p, self.d, self.backward = p, d, backward
+        self.p, self.d, self.backward, self.mx8 = p, d, backward, mx8
         self.route = moeq.RouteState(T, E, k, torch.device(DEV))
         self.bufs = dict(values=torch.empty(A, H, dtype=adt, device=DEV),
                          weights=torch.empty(T, k, dtype=torch.float32, device=DEV),
@@ -37,6 +37,9 @@ class Step:
         self.h = torch.empty(A, I, dtype=adt, device=DEV)
         self.y = torch.empty(A, H, dtype=adt, device=DEV)
         self.out = torch.empty(T, H, dtype=adt, device=DEV)
+        if mx8:
+            wsb = moeq.lib().mx8_workspace_bytes(A, max(H, I))
+            self.wsm = torch.empty(wsb, dtype=torch.uint8, device=DEV)
         if backward:
             self.gout = torch.zeros(T, H, dtype=adt, device=DEV)
             self.gy = torch.empty(A, H, dtype=adt, device=DEV)
@@ -50,9 +53,14 @@ class Step:
     def run(self):
         p, d, r = self.p, self.d, self.route
         moeq.moe_dispatch(d["x"], d["logits"], d["router_bias"], p["k"], r, self.bufs)
-        moeq.awq_grouped_swiglu(r, self.bufs["values"], d["gate"], d["up_arg"], p["clamp"],
-                                p["alpha"], p["up_offset"], self.h)
-        moeq.awq_grouped_down(r, self.h, d["down"], self.y)
+        if self.mx8:
+            moeq.mx8_grouped_swiglu(r, self.bufs["values"], d["gate"], p["clamp"], p["alpha"],
+                                    p["up_offset"], h=self.h, workspace=self.wsm)
+            moeq.mx8_grouped_down(r, self.h, d["down"], self.y, workspace=self.wsm)
+        else:
+            moeq.awq_grouped_swiglu(r, self.bufs["values"], d["gate"], d["up_arg"], p["clamp"],
+                                    p["alpha"], p["up_offset"], self.h)
+            moeq.awq_grouped_down(r, self.h, d["down"], self.y)
         moeq.moe_combine(r, self.y, self.bufs["weights"], self.out)
         if self.backward:
             moeq.moe_combine_backward(r, self.y, self.bufs["weights"], self.gout,
@@ -73,18 +81,19 @@ class Step:
         return {k: v.detach().cpu().clone() for k, v in t.items() if isinstance(v, torch.Tensor)}
 
 
-@pytest.mark.parametrize("name,T,backward", [
-    ("tiny", 16, True),        # fp32 activations: generic kernels
-    ("decode", 64, True),      # fused small dispatch, stream kernels
-    ("prefill", 1024, True),   # four-launch dispatch, register-decoded MFMA kernels
-    ("many", 1024, True),      # fp32 scales: warp-specialised MFMA kernels
-    ("mxfp4", 512, False),     # MXFP4 bank kernels
+@pytest.mark.parametrize("name,T,backward,mx8", [
+    ("tiny", 16, True, False),        # fp32 activations: generic kernels
+    ("decode", 64, True, False),      # fused small dispatch, stream kernels
+    ("prefill", 1024, True, False),   # four-launch dispatch, register-decoded MFMA kernels
+    ("many", 1024, True, False),      # fp32 scales: warp-specialised MFMA kernels
+    ("mxfp4", 512, False, False),     # MXFP4 bank kernels
+    ("mxfp4", 512, False, True),      # MXFP4 bank on the block-scaled MFMA (MXFP8 rows)
 ])
-def test_graph_replays_match_eager(name, T, backward):
-    print(f"[graph replay] {name} T={T} backward={backward}", flush=True)
+def test_graph_replays_match_eager(name, T, backward, mx8):
+    print(f"[graph replay] {name} T={T} backward={backward} mx8={mx8}", flush=True)
     p = make_inputs(CONFIGS[name], T=T)
     d = di.upload(p, DEV)
-    graph_step, eager_step = Step(p, d, backward), Step(p, d, backward)
+    graph_step, eager_step = Step(p, d, backward, mx8), Step(p, d, backward, mx8)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
