@@ -39,8 +39,13 @@
  *   orc_awq_swiglu_input_backward   finite differences of the gate/up + SwiGLU
  *                                   forward (fp32 activations)
  *   orc_e2m1_value, orc_e8m0_value  OCP MX element/scale tables
- *   orc_mxfp4_*                     golden byte, numpy matmul
- *   orc_moe_forward                 per-token dense float64 evaluation in numpy
+ *   orc_mxfp4_*                     golden byte, numpy matmul; a non-zero
+ *                                   bias distinct per (expert, row), exact
+ *   orc_moe_forward                 per-token dense float64 evaluation in numpy,
+ *                                   for AWQ cubes and for MXFP4 banks (dense
+ *                                   banks from the golden tables, gate and up
+ *                                   banks interleaved by the test, clamped and
+ *                                   one-sided SwiGLU, non-zero biases)
  * Parity unpinned by the pages (conventions only, frozen by golden values):
  *   the AWQ nibble permutation, the nibble order inside an MXFP4 byte, the
  *   row interleave of the fused gate/up bank, and the clamped-SwiGLU form.
