@@ -176,10 +176,41 @@ class AwqExperts:
     expert_start: int = 0
 
     def c(self) -> Experts:
+        self.validate()
         E, K, W8 = self.qweight.shape
         return Experts(FMT_AWQ, E, self.expert_start, K, W8 * 8, self.group_size,
                        _ptr(self.qweight), _ptr(self.qzeros), _ptr(self.scales),
                        _dt(self.scales), _ptr(self.bias), 0)
+
+    def validate(self) -> None:
+        """Shapes, dtypes and device of the payload tensors.  The C descriptor has
+        no dtype field for the bias (it is read in the scale dtype), so a bias of
+        another dtype or shape is rejected here rather than misread."""
+        qw, qz, sc, b = self.qweight, self.qzeros, self.scales, self.bias
+        if qw.dim() != 3 or qz.dim() != 3 or sc.dim() != 3:
+            raise MoeqError(ESHAPE, "AWQ qweight, qzeros and scales are rank-3 [E, ., .]")
+        if qw.dtype != torch.int32 or qz.dtype != torch.int32:
+            raise MoeqError(EDTYPE, "AWQ qweight and qzeros are int32 words")
+        if sc.dtype not in _TORCH_DT:
+            raise MoeqError(EDTYPE, f"AWQ scales must be fp32, fp16 or bf16, not {sc.dtype}")
+        E, K, W8 = qw.shape
+        g = int(self.group_size)
+        if g <= 0 or K % g:
+            raise MoeqError(ESHAPE, f"group size {g} does not divide in_features {K}")
+        N = W8 * 8
+        if tuple(qz.shape) != (E, K // g, W8):
+            raise MoeqError(ESHAPE, f"qzeros shape {tuple(qz.shape)} != {(E, K // g, W8)}")
+        if tuple(sc.shape) != (E, K // g, N):
+            raise MoeqError(ESHAPE, f"scales shape {tuple(sc.shape)} != {(E, K // g, N)}")
+        if b is not None:
+            if b.dtype != sc.dtype:
+                raise MoeqError(EDTYPE, f"AWQ bias dtype {b.dtype} differs from the scale "
+                                        f"dtype {sc.dtype} (the bias is held in the scale dtype)")
+            if tuple(b.shape) != (E, N):
+                raise MoeqError(ESHAPE, f"bias shape {tuple(b.shape)} != {(E, N)}")
+        devs = {t.device for t in (qw, qz, sc, b) if t is not None}
+        if len(devs) != 1:
+            raise MoeqError(EINVAL, "AWQ payload tensors live on different devices")
 
 
 @dataclasses.dataclass
@@ -192,10 +223,29 @@ class Mxfp4Bank:
     expert_start: int = 0
 
     def c(self) -> Experts:
+        self.validate()
         E, R, NB, _ = self.blocks.shape
         return Experts(FMT_MXFP4_BANK, E, self.expert_start, NB * 32, R, 32, _ptr(self.blocks),
                        None, _ptr(self.scales), BF16, _ptr(self.bias),
                        1 if self.interleaved_gate_up else 0)
+
+    def validate(self) -> None:
+        """Bank shapes and dtypes (native.rs validate): blocks u8 [E, R, C/32, 16],
+        E8M0 scales u8 [E, R, C/32], bias bf16 [E, R]."""
+        bl, sc, b = self.blocks, self.scales, self.bias
+        if bl.dim() != 4 or bl.shape[3] != 16:
+            raise MoeqError(ESHAPE, "MXFP4 blocks are [E, rows, cols/32, 16]")
+        if bl.dtype != torch.uint8 or sc.dtype != torch.uint8:
+            raise MoeqError(EDTYPE, "MXFP4 blocks and E8M0 scales are uint8")
+        E, R, NB, _ = bl.shape
+        if tuple(sc.shape) != (E, R, NB):
+            raise MoeqError(ESHAPE, f"MXFP4 scales shape {tuple(sc.shape)} != {(E, R, NB)}")
+        if b is None or b.dtype != torch.bfloat16:
+            raise MoeqError(EDTYPE, "MXFP4 banks carry a bf16 bias")
+        if tuple(b.shape) != (E, R):
+            raise MoeqError(ESHAPE, f"MXFP4 bias shape {tuple(b.shape)} != {(E, R)}")
+        if len({bl.device, sc.device, b.device}) != 1:
+            raise MoeqError(EINVAL, "MXFP4 bank tensors live on different devices")
 
 
 # ------------------------------------------------------------------ route
