@@ -177,6 +177,33 @@ moeq_status moe_dispatch(const void *x, moeq_dtype act, int32_t T, int32_t K,
                          moeq_route *route, void *stream);
 
 /*
+ * moe_dispatch_static -- for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): moe_dispatch with the route's row mappings in a fixed device
+ * array of the library instead of a caller workspace.  Same arguments, outputs,
+ * validation and kernels as moe_dispatch, except that `route` need not be
+ * bound: on success the call binds it to the array of the current device (the
+ * device of `stream`); on an error it leaves `route` untouched.
+ * Limit: moeq_route_workspace_bytes(T, E, top_k) <= MOEQ_STATIC_ROUTE_BYTES
+ * (4 MiB, e.g. T * top_k up to about 400k assignments at E = 512), else
+ * EWORKSPACE.  The array is one per GPU, held until the process ends, and
+ * shared by every call on that GPU: each call overwrites the row mappings of
+ * the previous one.  A route from this call therefore serves the calls that
+ * consume it (grouped projections, counts, combine, backward calls) when they
+ * are ordered before the next moe_dispatch_static on that GPU, e.g. enqueued on
+ * the same stream before it; calls that overlap on one GPU (other streams or
+ * threads without ordering) race.  Allocates and frees nothing; the first call
+ * on a device looks the array's address up once (hipGetSymbolAddress).
+ */
+#define MOEQ_STATIC_ROUTE_BYTES (4u << 20)
+
+moeq_status moe_dispatch_static(const void *x, moeq_dtype act, int32_t T, int32_t K,
+                                const float *logits, int32_t E, const float *expert_bias,
+                                int32_t top_k, void *values, float *weights,
+                                uint32_t *selected, uint32_t *row_experts, moeq_route *route,
+                                void *stream);
+
+/*
  * moe_dispatch_counts -- moe_exchange.rs MoeDispatchOps::moe_dispatch_counts:
  * rows per caller-declared contiguous range of global expert IDs, read from
  * the expert offsets only.  expert_prefix: host int64 [R+1], non-decreasing,

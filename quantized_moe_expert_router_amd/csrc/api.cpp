@@ -200,6 +200,16 @@ PackedOperand operand_of(const moeq_experts *w) {
 
 }  // namespace
 
+namespace moeq {
+moeq_status report_error(moeq_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+}  // namespace moeq
+
 extern "C" {
 
 const char *moeq_status_string(moeq_status s) {

@@ -58,6 +58,9 @@ enum ProjMode {
     PROJ_INPUT_VJP2 = 4, // out = in . Wg^T + in2 . Wu^T, AWQ
 };
 
+// Record a validation or device error for moeq_last_error() and return `st`.
+moeq_status report_error(moeq_status st, const char *fmt, ...);
+
 hipError_t launch_router(const float *logits, const float *bias, int T, int E, int k,
                          uint32_t *selected, float *weights, hipStream_t s);
 bool small_dispatch_fits(int T, int E, int k, size_t row_bytes, const void *x, const void *values);

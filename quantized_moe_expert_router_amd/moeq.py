@@ -26,7 +26,7 @@ _DT_TORCH = {v: k for k, v in _TORCH_DT.items()}
 
 # every symbol include/moeq.h declares
 EXPORTS = ("moeq_route_workspace_bytes", "moeq_route_bind", "moe_dispatch",
-           "moe_dispatch_counts", "awq_grouped_swiglu", "awq_grouped_down", "moe_combine",
+           "moe_dispatch_static", "moe_dispatch_counts", "awq_grouped_swiglu", "awq_grouped_down", "moe_combine",
            "awq_input_backward", "moe_combine_backward", "moe_dispatch_backward",
            "moe_dispatch_weights_backward", "awq_swiglu_input_backward_workspace_bytes",
            "awq_swiglu_input_backward", "awq_expert_workspace_bytes", "awq_expert_forward",
@@ -85,6 +85,8 @@ def lib():
     L.moe_dispatch.restype = C.c_int
     L.moe_dispatch.argtypes = [vp, C.c_int, i32, i32, vp, i32, vp, i32, vp, vp, vp, vp,
                                C.POINTER(Route), vp]
+    L.moe_dispatch_static.restype = C.c_int
+    L.moe_dispatch_static.argtypes = L.moe_dispatch.argtypes
     L.moe_dispatch_counts.restype = C.c_int
     L.moe_dispatch_counts.argtypes = [C.POINTER(Route), vp, i32, vp, vp]
     L.awq_grouped_swiglu.restype = C.c_int
@@ -303,6 +305,46 @@ def moe_dispatch(x: torch.Tensor, logits: torch.Tensor, expert_bias: Optional[to
     _check(lib().moe_dispatch(_ptr(x), _dt(x), T, K, _ptr(logits), E, _ptr(expert_bias), top_k,
                               _ptr(out["values"]), _ptr(out["weights"]), _ptr(out["selected"]),
                               _ptr(out["row_experts"]), C.byref(route.c), _stream(x.device)))
+    out["route"] = route
+    return out
+
+
+class StaticRoute:
+    """A moeq_route bound by moe_dispatch_static to the library's fixed device
+    array: valid until the next moe_dispatch_static on the same GPU."""
+
+    def __init__(self, device):
+        self.c = Route()
+        self.device = torch.device(device)
+        self.T = self.E = self.top_k = 0
+
+    @property
+    def A(self) -> int:
+        return self.T * self.top_k
+
+
+def moe_dispatch_static(x: torch.Tensor, logits: torch.Tensor,
+                        expert_bias: Optional[torch.Tensor], top_k: int,
+                        out: Optional[dict] = None, route: Optional[StaticRoute] = None):
+    """moe_dispatch with the route in the library's fixed per-GPU array (no route
+    workspace).  Returns the same dict as moe_dispatch, with a StaticRoute."""
+    T, K = x.shape
+    E = logits.shape[1]
+    A = T * top_k
+    if out is None:
+        out = dict(values=torch.empty(A, K, dtype=x.dtype, device=x.device),
+                   weights=torch.empty(T, top_k, dtype=torch.float32, device=x.device),
+                   selected=torch.empty(T, top_k, dtype=torch.int32, device=x.device),
+                   row_experts=torch.empty(A, dtype=torch.int32, device=x.device))
+    if logits.dtype != torch.float32 or (expert_bias is not None and expert_bias.dtype != torch.float32):
+        raise MoeqError(EDTYPE, "logits and expert bias are fp32")
+    if route is None:
+        route = StaticRoute(x.device)
+    _check(lib().moe_dispatch_static(_ptr(x), _dt(x), T, K, _ptr(logits), E, _ptr(expert_bias),
+                                     top_k, _ptr(out["values"]), _ptr(out["weights"]),
+                                     _ptr(out["selected"]), _ptr(out["row_experts"]),
+                                     C.byref(route.c), _stream(x.device)))
+    route.T, route.E, route.top_k = T, E, top_k
     out["route"] = route
     return out
 
