@@ -81,6 +81,8 @@ def parse():
     ap.add_argument("--kernel-launches", type=int, default=0,
                     help="launches per kernel-timing graph (default: replicas x ceil(16/R))")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured MFMA and HBM peaks")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -498,6 +500,84 @@ def measure_forward(cfg, args, steps, warmup, mx8=False):
         })
 
 
+def measured_peaks():
+    """Peaks measured on this GPU beside the published ones: a dense bf16 MFMA
+    loop on register operands (both MFMA shapes, 1, 2 and 4 waves per SIMD, the
+    best), a streaming HBM read of 4 GiB, and a 1 GiB device copy (read + write)."""
+    import ctypes as C
+    import torch
+    lib = C.CDLL(os.path.join(ROOT, "quantized_moe_expert_router_amd", "csrc",
+                              "libmoeq_peaks.so"))
+    lib.moeq_peak_mfma_bf16.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p,
+                                        C.c_void_p]
+    lib.moeq_peak_read.argtypes = [C.c_void_p, C.c_size_t, C.c_int, C.c_void_p, C.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = C.c_void_p(stream.cuda_stream)
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) * 1e-3
+            best = t if best is None else min(best, t)
+        return best
+
+    res = {}
+    blocks, iters = 256 * 4, 200
+    out = torch.empty(blocks * 64 * 16, dtype=torch.float32, device="cuda:0")
+    for shape, flop in ((0, 16384), (1, 32768)):
+        best = 0.0
+        for waves in (4, 8, 16):
+            def run():
+                rc = lib.moeq_peak_mfma_bf16(blocks, waves, iters, shape,
+                                             C.c_void_p(out.data_ptr()), sp)
+                assert rc == 0, rc
+            t = timed(run)
+            best = max(best, blocks * waves * iters * 8 * flop / t / 1e12)
+        res["mfma_bf16_16x16x32_tflops" if shape == 0 else "mfma_bf16_32x32x16_tflops"] = round(best, 1)
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    buf.fill_(1)
+    rblocks = 256 * 8
+    rout = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda:0")
+
+    def read():
+        rc = lib.moeq_peak_read(C.c_void_p(buf.data_ptr()), nbytes, rblocks,
+                                C.c_void_p(rout.data_ptr()), sp)
+        assert rc == 0, rc
+    res["hbm_read_gbs"] = round(nbytes / timed(read) / 1e9, 1)
+    half = buf[: 1 << 30]
+    dst = buf[1 << 30: 2 << 30]
+    res["hbm_copy_gbs"] = round(2 * (1 << 30) / timed(lambda: dst.copy_(half)) / 1e9, 1)
+    del buf, out, rout
+    torch.cuda.empty_cache()
+    res["method"] = ("best of 3 HIP-event-timed launches; MFMA: 1024 blocks x 4/8/16 waves, "
+                     "200 x 8 MFMAs per wave on registers; read: 4 GiB by 2048 blocks, "
+                     "16-byte loads; copy: torch 1 GiB device copy, bytes read + written")
+    return res
+
+
+def with_measured(rl, peaks):
+    """Add the fraction of the measured peak of the same kind to a roofline."""
+    if not peaks:
+        return rl
+    if rl["bound"] == "hbm":
+        ref = peaks["hbm_read_gbs"]
+    elif rl["peak"] == BF16_PEAK_TFLOPS:
+        ref = max(peaks["mfma_bf16_16x16x32_tflops"], peaks["mfma_bf16_32x32x16_tflops"])
+    else:
+        return rl
+    rl["measured_peak"] = ref
+    rl["frac_of_measured"] = round(rl["achieved"] / ref, 4)
+    return rl
+
+
 def release(torch, m):
     m.pop("wl", None)
     torch.cuda.synchronize()
@@ -739,8 +819,11 @@ def main():
         print("--path mx8 runs the MXFP4 bank workload (--config mxfp4)", file=sys.stderr)
         sys.exit(2)
 
+    peaks = None if args.no_peaks else measured_peaks()
     head = measure_forward(cfg, args, args.steps, args.warmup, mx8=mx8)
     r = head["result"]
+    with_measured(head["roofline"], peaks)
+    with_measured(r["roofline_down"], peaks)
     res = {
         "metric": METRIC_MX8 if mx8 else METRIC, "value": r["tokens_per_s"], "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
@@ -763,8 +846,12 @@ def main():
             m = measure_forward(CONFIGS[name], args, min(args.steps, 100),
                                 min(args.warmup, 10))
             others[name] = m["result"]
+            with_measured(others[name]["roofline_gate_up"], peaks)
+            with_measured(others[name]["roofline_down"], peaks)
             release(torch, m)
         res["workloads"] = others
+    if peaks:
+        res["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(res), flush=True)

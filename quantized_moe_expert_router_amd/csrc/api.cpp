@@ -73,8 +73,8 @@ bool route_layout(int32_t T, int32_t E, int32_t k, Layout *L) {
     o += align256(sizeof(int32_t) * (bb ? bb : 1));
     L->off_tiles = o;
     o += align256(sizeof(int32_t) * ((size_t)E + 1));
-    L->off_tile_expert = o;  // m-tiles: at most ceil(A / kTileRows) + E
-    o += align256(sizeof(int32_t) * ((A + kTileRows - 1) / kTileRows + (size_t)E));
+    L->off_tile_expert = o;  // tile_expert then tile_order, tile_cap(A, E) each
+    o += align256(sizeof(int32_t) * 2 * (size_t)tile_cap((long)A, E));
     L->total = o;
     return true;
 }
@@ -369,6 +369,7 @@ moeq_status awq_grouped_swiglu(const moeq_route *route, const void *values, moeq
     p.offsets = route->expert_offsets;
     p.tile_offsets = route->tile_offsets;
     p.tile_expert = route->tile_expert;
+    p.tile_order = route->tile_expert + tile_cap((long)route->T * route->top_k, route->E);
     p.rows = A;
     p.E = route->E;
     p.act = act;
@@ -404,6 +405,7 @@ moeq_status awq_grouped_down(const moeq_route *route, const void *h, moeq_dtype 
     p.offsets = route->expert_offsets;
     p.tile_offsets = route->tile_offsets;
     p.tile_expert = route->tile_expert;
+    p.tile_order = route->tile_expert + tile_cap((long)route->T * route->top_k, route->E);
     p.rows = A;
     p.E = route->E;
     p.act = act;
@@ -462,6 +464,8 @@ moeq_status awq_input_backward(const moeq_route *route, const void *grad, moeq_d
     p.offsets = route ? route->expert_offsets : nullptr;
     p.tile_offsets = route ? route->tile_offsets : nullptr;
     p.tile_expert = route ? route->tile_expert : nullptr;
+    p.tile_order = route ? route->tile_expert + tile_cap((long)route->T * route->top_k, route->E)
+                         : nullptr;
     p.rows = rows;
     p.E = route ? route->E : 1;
     p.act = gdt;
@@ -575,6 +579,7 @@ moeq_status awq_swiglu_input_backward(const moeq_route *route, const void *value
     p.offsets = route->expert_offsets;
     p.tile_offsets = route->tile_offsets;
     p.tile_expert = route->tile_expert;
+    p.tile_order = route->tile_expert + tile_cap((long)route->T * route->top_k, route->E);
     p.rows = A;
     p.E = route->E;
     p.act = act;
@@ -827,6 +832,7 @@ moeq_status awq_expert_forward(const void *x, moeq_dtype act, int32_t rows,
     p.offsets = route.expert_offsets;
     p.tile_offsets = route.tile_offsets;
     p.tile_expert = route.tile_expert;
+    p.tile_order = route.tile_expert + tile_cap((long)route.T * route.top_k, route.E);
     p.rows = rows;
     p.E = w->experts;
     p.act = act;
@@ -873,6 +879,7 @@ moeq_status awq_expert_input_backward(const void *grad, moeq_dtype gdt, int32_t 
     p.offsets = route.expert_offsets;
     p.tile_offsets = route.tile_offsets;
     p.tile_expert = route.tile_expert;
+    p.tile_order = route.tile_expert + tile_cap((long)route.T * route.top_k, route.E);
     p.rows = rows;
     p.E = w->experts;
     p.act = gdt;
@@ -892,7 +899,7 @@ size_t frozen_awq_workspace_bytes(int32_t rows) {
     if (rows < 0) return 0;
     // offsets [2], m-tile prefix [2], expert of each m-tile
     return align256(2 * sizeof(int32_t)) * 2 +
-           align256(sizeof(int32_t) * ((size_t)(rows + kTileRows - 1) / kTileRows + 1));
+           align256(sizeof(int32_t) * 2 * (size_t)tile_cap(rows, 1));
 }
 
 moeq_status frozen_awq_forward(const void *x, moeq_dtype act, int32_t rows,
@@ -928,6 +935,7 @@ moeq_status frozen_awq_forward(const void *x, moeq_dtype act, int32_t rows,
     p.offsets = offsets;
     p.tile_offsets = tile_offsets;
     p.tile_expert = tile_expert;
+    p.tile_order = tile_expert + tile_cap(rows, 1);
     p.rows = rows;
     p.E = 1;
     p.act = act;

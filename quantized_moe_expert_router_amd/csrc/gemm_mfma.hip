@@ -47,6 +47,7 @@ struct StreamArgs {
     int parts;                // column parts per expert (blocks per expert)
     int E;                    // experts
     int xcd_pairs;            // 1: the parts of an expert share an XCD (see kernel)
+    int max_rows;             // > 0: experts with more rows are left to an m-tile kernel
     int vec_out;              // 1: out (and out2, dh) 16-byte aligned: one vector per row of 8 columns
     const uint32_t *qw[2];
     const uint32_t *qz[2];
@@ -110,6 +111,7 @@ void awq_stream_kernel(StreamArgs a) {
     }
     const int r0 = a.offsets[e], r1 = a.offsets[e + 1];
     if (r1 <= r0) return;  // untouched expert: no weight bytes are read
+    if (a.max_rows > 0 && r1 - r0 > a.max_rows) return;  // a heavy expert: m-tile kernel
     // wave roles as scalars: keeps every K offset (buffer soffset) in SGPRs
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int q = wv % KSPLIT, unit = wv / KSPLIT;  // unit = (set, strip)
@@ -421,9 +423,15 @@ hipError_t launch_stream(const StreamArgs &a, int E, int ksplit, int rt, int dep
         MOEQ_STREAM(2, 1, 2, 4)
         MOEQ_STREAM(2, 1, 1, 0)
     }
+    if constexpr (NSETS * SPW * 2 <= 8) {  // two row tiles: at most two waves per SIMD
+        MOEQ_STREAM(2, 2, 2, 4)
+    }
     MOEQ_STREAM(1, 1, 4, 4)
     MOEQ_STREAM(1, 1, 2, 4)
     MOEQ_STREAM(1, 1, 1, 0)
+    if constexpr (NSETS * SPW <= 8) {
+        MOEQ_STREAM(1, 2, 2, 4)
+    }
     MOEQ_STREAM(1, 2, 1, 0)
 #undef MOEQ_STREAM
     return hipErrorInvalidValue;
@@ -459,9 +467,41 @@ bool stream_fits(const ProjProblem &p) {
     return rows_per_expert <= limit;
 }
 
+// max_rows > 0: the light-expert half of a split launch -- only experts with
+// 1..max_rows rows (at most 32: one pass of two 16-row tiles), the rest left to
+// an m-tile kernel.
+// Skewed routing with few rows per expert on average (more than the stream
+// kernel's 8, at most 64): experts with at most kSplitRows rows stream their
+// weights, the heavier ones run on an m-tile kernel that skips the light ones.
+// A light expert's m-tile costs an m-tile kernel nearly as much as a full one
+// (its per-step decode and barriers do not shrink with the rows), so on the
+// many-expert workload the light experts' blocks took most of the call.
+constexpr int kSplitRows = 32;
+
+int split_rows() {
+    if (const char *v = getenv("MOEQ_SPLIT_ROWS")) {  // tuning override: 16 or 32
+        const int x = atoi(v);
+        if (x == 16 || x == 32) return x;
+    }
+    return kSplitRows;
+}
+
+bool split_fits(const ProjProblem &p) {
+    if (const char *v = getenv("MOEQ_SPLIT")) {  // tuning override: 0 disables
+        if (atoi(v) == 0) return false;
+    }
+    if (p.act != MOEQ_BF16 || p.w0.format != MOEQ_FMT_AWQ || !p.offsets || !p.tile_offsets)
+        return false;
+    if (p.w0.N % 128 != 0 || p.w0.K % 32 != 0 || p.w0.g % 32 != 0) return false;
+    if ((size_t)p.rows * p.w0.K * 2 >= ((size_t)1 << 31)) return false;
+    const double rows_per_expert = (double)p.rows / (double)p.E;
+    return rows_per_expert > 8.0 && rows_per_expert <= 64.0;
+}
+
 template <int NSETS>
-hipError_t run_stream(const ProjProblem &p, hipStream_t s) {
+hipError_t run_stream(const ProjProblem &p, hipStream_t s, int max_rows = 0) {
     StreamArgs a{};
+    a.max_rows = max_rows;
     a.in = static_cast<const __bf16 *>(p.in);
     a.out = static_cast<__bf16 *>(p.out);
     a.offsets = p.offsets;
@@ -482,8 +522,10 @@ hipError_t run_stream(const ProjProblem &p, hipStream_t s) {
     a.dh = static_cast<const __bf16 *>(p.in2);
     a.out2 = static_cast<__bf16 *>(p.out2);
     const int strips = a.W / 16;
-    // rows: one 16-row tile unless experts average more than 8 rows
-    const int rt = ((double)p.rows / (double)p.E) <= 8.0 ? 1 : 2;
+    // rows: one 16-row tile unless experts average more than 8 rows (or, split,
+    // may hold more than 16)
+    const int rt = max_rows > 0 ? (max_rows > 16 ? 2 : 1)
+                                : (((double)p.rows / (double)p.E) <= 8.0 ? 1 : 2);
     // columns: a block's part is as wide as possible while E * parts still
     // covers the 256 CUs; two operand sets take 3-strip parts, one set 8
     int spw;
@@ -491,6 +533,9 @@ hipError_t run_stream(const ProjProblem &p, hipStream_t s) {
         spw = strips % 3 == 0 ? 3 : (strips % 2 == 0 ? 2 : 1);
     else
         spw = strips % 8 == 0 ? 8 : (strips % 4 == 0 ? 4 : (strips % 2 == 0 ? 2 : 1));
+    // split launches (light experts only, fp32 scales on the many-expert workload
+    // measured): one-strip parts, so the blocks spread over more CUs
+    if (max_rows > 0 && NSETS == 2) spw = 1;
     if (const char *v = getenv("MOEQ_STREAM_SPW")) {  // tuning override (launch shape only)
         const int x = atoi(v);
         if ((x == 1 || x == 2 || x == 3 || x == 4 || x == 8) && strips % x == 0) spw = x;
@@ -498,14 +543,15 @@ hipError_t run_stream(const ProjProblem &p, hipStream_t s) {
     // K split: two ways when the block stays within 12 waves (3 per SIMD, all
     // unspilled) and each half is whole groups
     int ksplit = (NSETS * spw * 2 <= 12 && (a.K / a.g) % 2 == 0) ? 2 : 1;
-    if (rt == 2) ksplit = 1;
+    if (rt == 2 && (max_rows == 0 || NSETS * spw * 2 > 8)) ksplit = 1;
+    if (rt == 2 && NSETS * spw > 8) return hipErrorInvalidValue;  // not instantiated
     if (const char *v = getenv("MOEQ_STREAM_KSPLIT")) {
         const int x = atoi(v);
-        if ((x == 1 || x == 2) && NSETS * spw * x <= 12 && a.K % (32 * x) == 0 && rt == 1)
+        if ((x == 1 || x == 2) && NSETS * spw * x <= (rt == 1 ? 12 : 8) && a.K % (32 * x) == 0)
             ksplit = x;
     }
     // the pipelined variant needs 128-row groups and group-aligned K slices
-    int depth = (rt == 1 && a.g == 128 && (a.K / ksplit) % a.g == 0) ? 2 : 1;
+    int depth = ((rt == 1 || max_rows > 0) && a.g == 128 && (a.K / ksplit) % a.g == 0) ? 2 : 1;
     if (const char *v = getenv("MOEQ_STREAM_DEPTH")) {
         const int x = atoi(v);
         if (x == 1 || (depth > 1 && (x == 2 || x == 4))) depth = x;
@@ -550,6 +596,17 @@ hipError_t launch_fast_swiglu(const ProjProblem &p, hipStream_t s, bool *handled
         *handled = true;
         return run_stream<2>(p, s);
     }
+    if (split_fits(p)) {
+        ProjProblem heavy = p;
+        heavy.split_rows = split_rows();
+        const bool wave = wave_fits(heavy);
+        if (wave || ws_fits(heavy)) {
+            *handled = true;
+            const hipError_t err = run_stream<2>(p, s, split_rows());
+            if (err != hipSuccess) return err;
+            return wave ? launch_wave(heavy, s) : launch_ws(heavy, s);
+        }
+    }
     if (wave_fits(p)) {
         *handled = true;
         return launch_wave(p, s);
@@ -576,6 +633,17 @@ hipError_t launch_fast_plain(const ProjProblem &p, hipStream_t s, bool *handled)
     if (stream_fits(p)) {
         *handled = true;
         return run_stream<1>(p, s);
+    }
+    if (split_fits(p)) {
+        ProjProblem heavy = p;
+        heavy.split_rows = split_rows();
+        const bool wave = wave_fits(heavy);
+        if (wave || ws_fits(heavy)) {
+            *handled = true;
+            const hipError_t err = run_stream<1>(p, s, split_rows());
+            if (err != hipSuccess) return err;
+            return wave ? launch_wave(heavy, s) : launch_ws(heavy, s);
+        }
     }
     if (wave_fits(p)) {
         *handled = true;

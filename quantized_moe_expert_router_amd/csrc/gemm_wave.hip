@@ -63,6 +63,7 @@ struct WaveArgs {
     int E, K, W, g;
     int groups;  // 128-column groups (16 word columns)
     int nblk;    // blocks per m-tile
+    int min_rows;  // > 0: experts with at most this many rows are left to another kernel
     int Nout;
     const uint32_t *qw[2];
     const uint32_t *qz[2];
@@ -104,6 +105,7 @@ void awq_wave_kernel(WaveArgs a) {
     const int cg = NSETS == 2 ? nb * (kWaves / 4) + (wv >> 2) : nb * (kWaves / 2) + (wv >> 1);
     const bool active = cg < a.groups;  // inactive waves still load A and meet every barrier
     const int e = a.tile_expert[mt];
+    if (a.offsets[e + 1] - a.offsets[e] <= a.min_rows) return;  // a light expert: streamed
     const int m0 = a.offsets[e] + (mt - a.tile_offsets[e]) * kWaveRows;
     const int m1 = min(m0 + kWaveRows, a.offsets[e + 1]);
 
@@ -366,6 +368,7 @@ hipError_t run_wave(const ProjProblem &p, hipStream_t s) {
     a.out = static_cast<__bf16 *>(p.out);
     a.offsets = p.offsets;
     a.tile_offsets = p.tile_offsets;
+    a.min_rows = p.split_rows;
     a.tile_expert = p.tile_expert;
     a.E = p.E;
     a.K = p.w0.K;

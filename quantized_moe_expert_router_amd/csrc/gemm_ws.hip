@@ -32,7 +32,10 @@
 // Blocks: m-tiles dealt round-robin to the eight XCDs (block b runs on XCD
 // b % 8), so a heavy expert's m-tiles spread over all of them.  Contiguous
 // ranges per XCD (an expert's m-tiles sharing one L2) were 5% slower on the
-// many-expert workload, where a few experts hold most rows.
+// many-expert workload, where a few experts hold most rows.  The m-tiles are
+// taken in the route's scheduling order: every full tile first, the partial
+// ones (light experts, ragged ends) after, so the longest blocks start first
+// and the short ones fill in behind them.
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
@@ -62,8 +65,10 @@ struct WsArgs {
     const int32_t *offsets;
     const int32_t *tile_offsets;
     const int32_t *tile_expert;
+    const int32_t *tile_order;  // nullable: m-tiles in scheduling order (full ones first)
     int E, K, W, g;
     int nblk;  // blocks per m-tile
+    int min_rows;  // > 0: experts with at most this many rows are left to another kernel
     int Nout;
     const uint32_t *qw[2];
     const uint32_t *qz[2];
@@ -91,9 +96,12 @@ void awq_ws_kernel(WsArgs a) {
     const int per_xcd = (mtiles + 7) / 8;
     const int x = blockIdx.x % 8, idx = blockIdx.x / 8;
     const int local = idx / a.nblk, nb = idx % a.nblk;
-    const int mt = local * 8 + x;
-    if (local >= per_xcd || mt >= mtiles) return;
+    const int slot = local * 8 + x;
+    if (local >= per_xcd || slot >= mtiles) return;
+    // full m-tiles start first, partial ones after (longest first)
+    const int mt = a.tile_order ? a.tile_order[slot] : slot;
     const int e = a.tile_expert[mt];
+    if (a.offsets[e + 1] - a.offsets[e] <= a.min_rows) return;  // a light expert: streamed
     const int m0 = a.offsets[e] + (mt - a.tile_offsets[e]) * kRows;
     const int m1 = min(m0 + kRows, a.offsets[e + 1]);
     const int K = a.K, W = a.W, N = W * 8, g = a.g, G = K / g;
@@ -340,6 +348,8 @@ hipError_t run_ws(const ProjProblem &p, hipStream_t s) {
     a.offsets = p.offsets;
     a.tile_offsets = p.tile_offsets;
     a.tile_expert = p.tile_expert;
+    a.tile_order = p.tile_order;
+    a.min_rows = p.split_rows;
     a.E = p.E;
     a.K = p.w0.K;
     a.W = p.w0.N / 8;

@@ -14,6 +14,14 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 2048;
 constexpr int kTileRows = 128;                // rows per m-tile of the tiled projections
 
+// Most m-tiles of kTileRows rows that A rows in E experts can form.  A route's
+// tile list holds tile_expert[cap] followed by tile_order[cap]: the m-tiles
+// with every full tile (in m-tile order) before the partial ones, the order in
+// which the warp-specialised kernel schedules them (longest first).
+__host__ __device__ inline int tile_cap(long A, int E) {
+    return (int)((A + kTileRows - 1) / kTileRows) + E;
+}
+
 // One packed projection operand as the kernels see it (validated on the host).
 struct PackedOperand {
     int format;          // moeq_format
@@ -37,6 +45,7 @@ struct ProjProblem {
     const int32_t *offsets;
     const int32_t *tile_offsets;  // [E+1] m-tile prefix (route), nullable
     const int32_t *tile_expert;   // expert of each m-tile (route), nullable
+    const int32_t *tile_order;    // m-tiles, full ones first (route), nullable
     int rows;            // total rows (A)
     int E;               // experts in the grid
     int act;             // activation / gradient storage
@@ -47,6 +56,8 @@ struct ProjProblem {
     int mode;            // see ProjMode
     float clamp, alpha, up_offset;
     float gate_lo;       // lower clamp bound of the gate: -clamp, or -inf (one-sided variant)
+    int split_rows;      // > 0: experts with at most this many rows go to the weight-streaming
+                         // kernel, the m-tile kernels skip them (set by the kernel choice)
 };
 
 enum ProjMode {

@@ -326,10 +326,40 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
         __syncthreads();
         int tbase = 0;
         for (int w = 0; w < wv; ++w) tbase += wave_tot[w];
+        // scheduling order: every full m-tile (m-tile order), then the partial ones
+        const int nfull = v / kTileRows, npart = nt - nfull;
+        __syncthreads();
+        int fincl = nfull;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int n = __shfl_up(fincl, o);
+            if (lane >= o) fincl += n;
+        }
+        if (lane == kWave - 1) wave_tot[wv] = fincl;
+        __syncthreads();
+        int fbase = 0, ftotal = 0;
+        for (int w = 0; w < wv; ++w) fbase += wave_tot[w];
+        for (int w = 0; w < 16; ++w) ftotal += wave_tot[w];
+        __syncthreads();
+        int pincl = npart;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int n = __shfl_up(pincl, o);
+            if (lane >= o) pincl += n;
+        }
+        if (lane == kWave - 1) wave_tot[wv] = pincl;
+        __syncthreads();
+        int pbase = 0;
+        for (int w = 0; w < wv; ++w) pbase += wave_tot[w];
         if (blockIdx.x == 0) {
+            int32_t *tile_order_g = tile_expert_g + tile_cap(A, E);
             if (tid < E) {
-                tile_offsets_g[tid] = tbase + tincl - nt;
-                for (int t = 0; t < nt; ++t) tile_expert_g[tbase + tincl - nt + t] = tid;
+                const int first = tbase + tincl - nt;
+                tile_offsets_g[tid] = first;
+                for (int t = 0; t < nt; ++t) tile_expert_g[first + t] = tid;
+                const int fpos = fbase + fincl - nfull;
+                for (int t = 0; t < nfull; ++t) tile_order_g[fpos + t] = first + t;
+                if (npart) tile_order_g[ftotal + pbase + pincl - 1] = first + nfull;
             }
             if (tid == E - 1) tile_offsets_g[E] = tbase + tincl;
         }
@@ -497,12 +527,28 @@ __global__ __launch_bounds__(1024) void block_scan_kernel(int32_t *__restrict__ 
     __syncthreads();
     const int nt0 = (tot[0] + kTileRows - 1) / kTileRows, nt1 = (tot[1] + kTileRows - 1) / kTileRows;
     const int texcl = block_exclusive_scan_1024(nt0 + nt1, wave_tot);
+    // scheduling order: every full m-tile (m-tile order), then the partial ones
+    const int nf0 = tot[0] / kTileRows, nf1 = tot[1] / kTileRows;
+    const int np0 = nt0 - nf0, np1 = nt1 - nf1;
+    __syncthreads();
+    const int fexcl = block_exclusive_scan_1024(nf0 + nf1, wave_tot);
+    __syncthreads();
+    __shared__ int ftotal_s;
+    if (threadIdx.x == blockDim.x - 1) ftotal_s = fexcl + nf0 + nf1;
+    const int pexcl = block_exclusive_scan_1024(np0 + np1, wave_tot);
+    __syncthreads();
+    const int ftotal = ftotal_s;
+    int32_t *tile_order = tile_expert + tile_cap(A, E);
     for (int q = 0; q < 2; ++q) {
         const int e = 2 * (int)threadIdx.x + q;
         const int first = q == 0 ? texcl : texcl + nt0, n = q == 0 ? nt0 : nt1;
+        const int nf = q == 0 ? nf0 : nf1, np = q == 0 ? np0 : np1;
+        const int fpos = q == 0 ? fexcl : fexcl + nf0, ppos = q == 0 ? pexcl : pexcl + np0;
         if (e < E) {
             tile_offsets[e] = first;
             for (int t = 0; t < n; ++t) tile_expert[first + t] = e;
+            for (int t = 0; t < nf; ++t) tile_order[fpos + t] = first + t;
+            if (np) tile_order[ftotal + ppos] = first + nf;
         }
         if (e == E - 1) tile_offsets[E] = first + n;
     }
@@ -584,7 +630,10 @@ __global__ __launch_bounds__(256) void single_tiles_kernel(int rows, int32_t *__
         tile_offsets[0] = 0;
         tile_offsets[1] = nt;
     }
-    if (i < nt) tile_expert[i] = 0;
+    if (i < nt) {
+        tile_expert[i] = 0;
+        tile_expert[tile_cap(rows, 1) + i] = i;  // scheduling order: the m-tiles in order
+    }
 }
 
 hipError_t launch_single_tiles(int rows, int32_t *offsets, int32_t *tile_offsets,

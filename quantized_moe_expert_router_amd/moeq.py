@@ -284,6 +284,14 @@ class RouteState:
     def slot_pos(self) -> torch.Tensor:
         return self._view("slot_pos", self.A).view(self.T, self.top_k)
 
+    def tile_lists(self):
+        """Internal m-tile lists of the tiled kernels: (tile_offsets [E+1], tile_expert,
+        tile_order), the last two of length ceil(A/128) + E (entries past the
+        m-tile count are unused)."""
+        cap = (self.A + 127) // 128 + self.E
+        te = self._view("tile_expert", 2 * cap)
+        return self._view("tile_offsets", self.E + 1), te[:cap], te[cap:]
+
 
 # ------------------------------------------------------------------ calls
 def moe_dispatch(x: torch.Tensor, logits: torch.Tensor, expert_bias: Optional[torch.Tensor],

@@ -58,6 +58,45 @@ def test_dispatch_bit_exact_full_size(name):
     assert sum(moeq.moe_dispatch_counts(r, [0, p["E"]])) == p["T"] * p["k"]
 
 
+def expected_tile_lists(off):
+    """128-row m-tiles per expert, and their scheduling order: every full m-tile
+    in m-tile order, then each expert's partial last tile in expert order."""
+    rows = np.diff(off)
+    nt = (rows + 127) // 128
+    first = np.concatenate([[0], np.cumsum(nt)])
+    expert = np.repeat(np.arange(len(rows)), nt)
+    full = [first[e] + t for e in range(len(rows)) for t in range(rows[e] // 128)]
+    part = [first[e] + rows[e] // 128 for e in range(len(rows)) if rows[e] % 128]
+    return first, expert, np.array(full + part, np.int64)
+
+
+@pytest.mark.parametrize("name,T,E,k", [("prefill", None, None, None), ("many", None, None, None),
+                                        ("decode", None, None, None), ("mxfp4", None, None, None),
+                                        ("decode", 200, 64, 6), ("prefill", 700, 2048, 6)])
+def test_tile_lists(name, T, E, k):
+    """The m-tile lists both dispatch paths build for the tiled kernels: per-expert
+    prefix, expert of each m-tile, and the full-tiles-first scheduling order
+    (exact)."""
+    over = {kk: v for kk, v in (("T", T), ("E", E), ("k", k)) if v is not None}
+    cfg = dataclasses.replace(CONFIGS[name], **over)
+    if E is not None:
+        cfg = dataclasses.replace(cfg, router_bias="none")
+    p = make_inputs(cfg)
+    print(f"[tile lists] {name} T={p['T']} E={p['E']} k={p['k']}", flush=True)
+    d = di.upload(p, DEV)
+    disp = moeq.moe_dispatch(d["x"], d["logits"], d["router_bias"], p["k"])
+    torch.cuda.synchronize()
+    r = disp["route"]
+    off = r.expert_offsets.cpu().numpy()
+    first, expert, order = expected_tile_lists(off)
+    t_off, t_exp, t_ord = (t.cpu().numpy() for t in r.tile_lists())
+    n = int(first[-1])
+    np.testing.assert_array_equal(t_off, first)
+    np.testing.assert_array_equal(t_exp[:n], expert)
+    np.testing.assert_array_equal(t_ord[:n], order)
+    assert sorted(t_ord[:n].tolist()) == list(range(n))
+
+
 @pytest.mark.parametrize("T,E,k", [(700, 2048, 6), (513, 1024, 32), (257, 2048, 1)])
 def test_dispatch_many_experts_many_blocks(T, E, k):
     """Large-batch dispatch at the expert limit: several 256-token blocks with
@@ -418,3 +457,47 @@ def test_mxfp4_tiled_path_parity(T, E, k, H, I, edge_scales, kernel, monkeypatch
     assert np.array_equal(np.isnan(y_gpu), np.isnan(yr))
     keep = ~np.isnan(yr).any(axis=1)
     assert row_rel_err(y_gpu[keep], yr[keep]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("sdt,bias,kernel", [("bf16", False, "wave"), ("f32", True, "ws"),
+                                             ("f16", True, "ws")])
+def test_split_path_parity(sdt, bias, kernel, monkeypatch):
+    """Skewed routing at 8 < rows per expert <= 64: experts with at most 32 rows
+    run on the weight-streaming kernel, the heavier ones on an m-tile kernel
+    (register-decoded, or warp-specialised when it is switched off or the scales
+    are fp32), each skipping the other's experts.  Forward stages and the chain
+    input VJP against the oracle."""
+    if kernel == "ws":
+        monkeypatch.setenv("MOEQ_WAVE", "0")
+    cfg = dataclasses.replace(CONFIGS["decode"], T=384, E=64, k=4, H=512, I=256, sdt=sdt,
+                              awq_bias=bias)
+    p = make_inputs(cfg, seed=55)
+    rb = np.zeros(p["E"], np.float32)
+    rb[[3, 17, 40, 41, 63]] = [3.0, 2.5, 2.0, 1.5, 1.0]     # a few heavy experts
+    p["router_bias"] = rb
+    print(f"[split] sdt={sdt} bias={bias} kernel={kernel}", flush=True)
+    g = run_path(p)
+    check_dispatch(p, g)
+    rows = np.diff(g["offsets"])
+    assert rows.max() > 32 and 0 < rows[(rows > 0)].min() <= 32 and 8 < p["T"] * p["k"] / p["E"] <= 64
+    ref = oracle.moe_forward(p)
+    tol = TOL["bf16"]
+    assert row_rel_err(f64(g["h"], "bf16"), f64(ref["h"], "bf16")) <= tol
+    h_or = di.tensor(ref["h"], "bf16", DEV)
+    y_gpu = di.to_host(moeq.awq_grouped_down(g["route"], h_or, g["dev"]["down"]), "bf16")
+    assert row_rel_err(f64(y_gpu, "bf16"), f64(ref["y"], "bf16")) <= tol
+    assert row_rel_err(f64(g["out"], "bf16"), f64(ref["out"], "bf16")) <= tol
+    # the chain input VJP over the same split
+    A = p["T"] * p["k"]
+    grad = to_storage(np.random.default_rng(56).normal(0, 1, (A, p["H"])), "bf16")
+    d = g["dev"]
+    gv = moeq.awq_swiglu_input_backward(g["route"], g["disp"]["values"], d["gate"], d["up"],
+                                        d["down"], di.tensor(grad, "bf16", DEV))
+    torch.cuda.synchronize()
+    dh = oracle.awq_input_backward(grad, "bf16", ref["row_experts"], p["down_qw"],
+                                   p["down_qz"], p["down_s"], sdt, p["group"])
+    rv = oracle.awq_swiglu_input_backward(ref["values"], "bf16", ref["row_experts"],
+                                          (p["gate_qw"], p["gate_qz"], p["gate_s"], p["gate_b"]),
+                                          (p["up_qw"], p["up_qz"], p["up_s"], p["up_b"]), sdt,
+                                          p["group"], dh)
+    assert row_rel_err(f64(di.to_host(gv, "bf16"), "bf16"), f64(rv, "bf16")) <= tol
