@@ -747,8 +747,15 @@ def _counter_per_dispatch(d, counter, kernel_sub):
 
 
 def summarize_traffic(dirs, kernel_sub, title, alg_bytes_per_launch=None):
-    fetch, nf, names = _counter_per_dispatch(dirs[0], "FETCH_SIZE", kernel_sub)
-    write, nw, _ = _counter_per_dispatch(dirs[1], "WRITE_SIZE", kernel_sub)
+    """kernel_sub: one name substring, or several separated by '|' for a call
+    made of several kernels (their per-dispatch means add up)."""
+    fetch = write = 0.0
+    names, nf, nw = [], 0, 0
+    for sub in kernel_sub.split("|"):
+        f1, n1, nm1 = _counter_per_dispatch(dirs[0], "FETCH_SIZE", sub)
+        w1, n2, _ = _counter_per_dispatch(dirs[1], "WRITE_SIZE", sub)
+        fetch, write, nf, nw = fetch + f1, write + w1, nf + n1, nw + n2
+        names += nm1
     cf, _, _ = _counter_per_dispatch(dirs[2], "FETCH_SIZE", "copyBuffer")
     cw, _, _ = _counter_per_dispatch(dirs[3], "WRITE_SIZE", "copyBuffer")
     copy_bytes = 1 << 30      # bench.py --copy-probe-mib 1024: 1 GiB read and 1 GiB written
@@ -758,7 +765,8 @@ def summarize_traffic(dirs, kernel_sub, title, alg_bytes_per_launch=None):
         print(f"# {title}")
     print("# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; the factors scale them by what the")
     print(f"# same counters read for a plain copy of {copy_bytes} bytes each way.")
-    print(f"kernel: {names[0][:160]}")
+    for nm in names:
+        print(f"kernel: {nm[:160]}")
     print(f"dispatches_fetch: {nf}")
     print(f"dispatches_write: {nw}")
     print(f"fetch_kib_per_dispatch: {fetch:.1f}")

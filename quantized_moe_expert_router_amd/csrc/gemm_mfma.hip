@@ -185,30 +185,27 @@ void awq_stream_kernel(StreamArgs a) {
         if constexpr (SPG > 0) {
             // Branch-free pipeline: groups of SPG steps, steps unrolled, DEPTH
             // steps in flight in a fixed register ring (slot t % DEPTH).  Loads
-            // past the wave's K range get an out-of-range offset (the buffer
-            // unit returns zeros without a memory access), so every load is
-            // issued unconditionally and the wait counts stay exact.  Each issue
-            // is pinned by a scheduling barrier: the scheduler would otherwise
-            // sink the prefetch next to its use.
+            // past the wave's K range re-read its last step (clamped, in range,
+            // never consumed), so every load is issued unconditionally and the
+            // wait counts stay exact.  Each issue is pinned by a scheduling
+            // barrier: the scheduler would otherwise sink the prefetch next to
+            // its use.
             static_assert(SPG % DEPTH == 0 && SPG >= DEPTH, "ring must tile a group");
             uint32_t wd[DEPTH][8];
             bf16x8 av[DEPTH][RT];
-            constexpr int kOff = 0x40000000;  // beyond any cube: reads as zero
             auto issue_words = [&](int st, int kk) {
-                const bool on = kk < kend;
+                const int kc = kk < kend ? kk : kend - 32;
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    wd[st][i] = __builtin_amdgcn_raw_buffer_load_b32(
-                        rw, voff_w, on ? (kk + i) * W * 4 : kOff, 0);
+                    wd[st][i] = __builtin_amdgcn_raw_buffer_load_b32(rw, voff_w, (kc + i) * W * 4, 0);
                 __builtin_amdgcn_sched_barrier(0);
             };
             auto issue_rows = [&](int st, int kk) {
-                const bool on = kk < kend;
+                const int kc = kk < kend ? kk : kend - 32;
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
                     av[st][rt] = __builtin_bit_cast(
-                        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, voff_a[rt],
-                                                                      on ? kk * 2 : kOff, 0));
+                        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra, voff_a[rt], kc * 2, 0));
                 __builtin_amdgcn_sched_barrier(0);
             };
             const int gbeg = kbeg / g, gend = kend / g;
