@@ -68,11 +68,21 @@ typedef enum {
     MOEQ_EDEVICE = -7        /* HIP launch or copy failure                      */
 } moeq_status;
 
-typedef enum { MOEQ_F32 = 0, MOEQ_F16 = 1, MOEQ_BF16 = 2 } moeq_dtype;
+/* The *_RANGE_ enumerators below are not valid values.  They give each enum the
+ * whole int32 range, so that an unknown value from a caller is still a value of
+ * the type (in C++ a value outside an enum's range is undefined), which the
+ * validation then rejects with MOEQ_EDTYPE or MOEQ_EINVAL. */
+typedef enum {
+    MOEQ_F32 = 0, MOEQ_F16 = 1, MOEQ_BF16 = 2,
+    MOEQ_DTYPE_RANGE_MIN_ = -2147483647 - 1, MOEQ_DTYPE_RANGE_MAX_ = 2147483647
+} moeq_dtype;
 
 /* Packed payload tag (packed_experts.rs PackedExpertPayload): AWQ I32 words,
  * or an MXFP4 expert bank (native.rs ExpertLayout::Native). */
-typedef enum { MOEQ_FMT_AWQ = 0, MOEQ_FMT_MXFP4_BANK = 1 } moeq_format;
+typedef enum {
+    MOEQ_FMT_AWQ = 0, MOEQ_FMT_MXFP4_BANK = 1,
+    MOEQ_FMT_RANGE_MIN_ = -2147483647 - 1, MOEQ_FMT_RANGE_MAX_ = 2147483647
+} moeq_format;
 
 /*
  * Route state: the "private native row mappings" of moe_exchange.rs
@@ -159,7 +169,8 @@ typedef struct moeq_swiglu {
 /*
  * moe_dispatch -- moe_exchange.rs MoeDispatchOps::moe_dispatch / MoeDispatched.
  *   x        [T, K] act (F32 or BF16)          input rows
- *   logits   [T, E] fp32                        router logits
+ *   logits   [T, E] logit_dtype (F32 or BF16)   router logits; bf16 logits are
+ *                                               widened exactly to fp32 first
  *   expert_bias [E] fp32 or NULL                added to the logits (one fp32
  *                                               add) before selection and softmax
  * Outputs (A = T * top_k):
@@ -172,10 +183,10 @@ typedef struct moeq_swiglu {
  * Implemented for E <= 2048, top_k <= 32 (else EUNSUPPORTED).  T = 0: no-op.
  */
 moeq_status moe_dispatch(const void *x, moeq_dtype act, int32_t T, int32_t K,
-                         const float *logits, int32_t E, const float *expert_bias,
-                         int32_t top_k, void *values, float *weights,
-                         uint32_t *selected, uint32_t *row_experts,
-                         moeq_route *route, void *stream);
+                         const void *logits, moeq_dtype logit_dtype, int32_t E,
+                         const float *expert_bias, int32_t top_k, void *values, float *weights,
+                         uint32_t *selected, uint32_t *row_experts, moeq_route *route,
+                         void *stream);
 
 /*
  * moe_dispatch_static -- for callers that cannot allocate device memory (code
@@ -199,10 +210,10 @@ moeq_status moe_dispatch(const void *x, moeq_dtype act, int32_t T, int32_t K,
 #define MOEQ_STATIC_ROUTE_BYTES (4u << 20)
 
 moeq_status moe_dispatch_static(const void *x, moeq_dtype act, int32_t T, int32_t K,
-                                const float *logits, int32_t E, const float *expert_bias,
-                                int32_t top_k, void *values, float *weights,
-                                uint32_t *selected, uint32_t *row_experts, moeq_route *route,
-                                void *stream);
+                                const void *logits, moeq_dtype logit_dtype, int32_t E,
+                                const float *expert_bias, int32_t top_k, void *values,
+                                float *weights, uint32_t *selected, uint32_t *row_experts,
+                                moeq_route *route, void *stream);
 
 /*
  * moe_dispatch_counts -- moe_exchange.rs MoeDispatchOps::moe_dispatch_counts:

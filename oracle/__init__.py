@@ -18,7 +18,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+_SANITIZE = os.environ.get("MOEQ_ORACLE_SANITIZE") == "1"
+_LIB_PATH = os.path.join(_HERE, "libmoe_oracle_san.so" if _SANITIZE else "libmoe_oracle.so")
 _lib = None
 
 DT = {"f32": 0, "f16": 1, "bf16": 2}
@@ -31,7 +32,7 @@ def _load():
         return _lib
     if not os.path.exists(_LIB_PATH):
         from . import build as _b
-        _b.build()
+        _b.build(sanitize=_SANITIZE)
     lib = C.CDLL(_LIB_PATH)
     vp, i32, u32p = C.c_void_p, C.c_int, C.c_void_p
     lib.orc_round_f16.restype = C.c_uint16

@@ -262,9 +262,10 @@ moeq_status moeq_route_bind(moeq_route *route, void *workspace, size_t bytes, in
 }
 
 moeq_status moe_dispatch(const void *x, moeq_dtype act, int32_t T, int32_t K,
-                         const float *logits, int32_t E, const float *expert_bias,
-                         int32_t top_k, void *values, float *weights, uint32_t *selected,
-                         uint32_t *row_experts, moeq_route *route, void *stream) {
+                         const void *logits, moeq_dtype logit_dtype, int32_t E,
+                         const float *expert_bias, int32_t top_k, void *values, float *weights,
+                         uint32_t *selected, uint32_t *row_experts, moeq_route *route,
+                         void *stream) {
     moeq_status st = check_route(route);
     if (st != MOEQ_OK) return st;
     if (route->T != T || route->E != E || route->top_k != top_k)
@@ -272,6 +273,9 @@ moeq_status moe_dispatch(const void *x, moeq_dtype act, int32_t T, int32_t K,
                     route->T, route->E, route->top_k, T, E, top_k);
     if (K < 1) return fail(MOEQ_EINVAL, "K must be positive");
     if (!valid_dtype(act)) return fail(MOEQ_EDTYPE, "unknown activation dtype %d", (int)act);
+    if (logit_dtype != MOEQ_F32 && logit_dtype != MOEQ_BF16)
+        return fail(MOEQ_EDTYPE, "router logits are fp32 or bf16, got dtype %d", (int)logit_dtype);
+    const bool lbf16 = logit_dtype == MOEQ_BF16;
     if (E > kMaxExperts || top_k > kMaxTopK)
         return fail(MOEQ_EUNSUPPORTED, "router implements E <= %d and top_k <= %d", kMaxExperts,
                     kMaxTopK);
@@ -283,11 +287,13 @@ moeq_status moe_dispatch(const void *x, moeq_dtype act, int32_t T, int32_t K,
         return fail(MOEQ_EINVAL, "NULL tensor pointer");
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (small_dispatch_fits(T, E, top_k, row_bytes, x, values))  // one launch for small batches
-        return device_status(launch_dispatch_small(x, row_bytes, logits, expert_bias, T, E, top_k,
+        return device_status(launch_dispatch_small(x, row_bytes, logits, lbf16, expert_bias, T, E,
+                                                   top_k,
                                                    values, weights, selected, row_experts, route,
                                                    s),
                              "dispatch");
-    if ((st = device_status(launch_router(logits, expert_bias, T, E, top_k, selected, weights, s),
+    if ((st = device_status(launch_router(logits, lbf16, expert_bias, T, E, top_k, selected,
+                                          weights, s),
                             "router")) != MOEQ_OK)
         return st;
     if ((st = device_status(launch_dispatch_index(selected, T, E, top_k, route, row_experts, s),

@@ -553,6 +553,12 @@ hipError_t run_stream(const ProjProblem &p, hipStream_t s, int max_rows = 0) {
         const int x = atoi(v);
         if (x == 1 || (depth > 1 && (x == 2 || x == 4))) depth = x;
     }
+    // two row tiles exist at depths 1 and 2, and split over K only at depth 2
+    // (group sizes other than 128 run unpipelined, hence unsplit)
+    if (rt == 2) {
+        if (depth == 4) depth = 2;
+        if (ksplit == 2 && (depth != 2 || NSETS * spw * 2 > 8)) ksplit = 1;
+    }
     a.parts = strips / spw;
     a.E = p.E;
     a.vec_out = (((uintptr_t)p.out | (uintptr_t)p.out2 | (uintptr_t)p.in2) % 16) == 0;

@@ -95,13 +95,21 @@ struct RouteRaw {
     float v[EPL], b[EPL];
 };
 
-template <int LANES, int EPL>
-__device__ __forceinline__ void route_load(const float *__restrict__ logits,
+// LBF16: bf16 logits, widened exactly to fp32 (the bits moved to the high half).
+template <int LANES, int EPL, bool LBF16>
+__device__ __forceinline__ void route_load(const void *__restrict__ logits,
                                            const float *__restrict__ bias, int t, int E, int r,
                                            RouteRaw<EPL> &raw) {
-    const float *row = logits + (size_t)t * E;
+    if constexpr (LBF16) {
+        const uint16_t *row = static_cast<const uint16_t *>(logits) + (size_t)t * E;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) raw.v[i] = row[min(r + LANES * i, E - 1)];
+        for (int i = 0; i < EPL; ++i)
+            raw.v[i] = __uint_as_float((uint32_t)row[min(r + LANES * i, E - 1)] << 16);
+    } else {
+        const float *row = static_cast<const float *>(logits) + (size_t)t * E;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) raw.v[i] = row[min(r + LANES * i, E - 1)];
+    }
     if (bias) {
 #pragma unroll
         for (int i = 0; i < EPL; ++i) raw.b[i] = bias[min(r + LANES * i, E - 1)];
@@ -165,18 +173,18 @@ __device__ __forceinline__ void route_select(const RouteRaw<EPL> &raw, bool has_
     *w_out = (float)(ex / den);
 }
 
-template <int LANES, int EPL>
-__device__ __forceinline__ void route_token(const float *__restrict__ logits,
+template <int LANES, int EPL, bool LBF16>
+__device__ __forceinline__ void route_token(const void *__restrict__ logits,
                                             const float *__restrict__ bias, int t, int E, int k,
                                             int r, int group_base_lane, int *sel_out,
                                             float *w_out) {
     RouteRaw<EPL> raw;
-    route_load<LANES, EPL>(logits, bias, t, E, r, raw);
+    route_load<LANES, EPL, LBF16>(logits, bias, t, E, r, raw);
     route_select<LANES, EPL>(raw, bias != nullptr, E, k, r, group_base_lane, sel_out, w_out);
 }
 
-template <int LANES, int EPL>
-__global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ logits,
+template <int LANES, int EPL, bool LBF16>
+__global__ __launch_bounds__(256) void router_kernel(const void *__restrict__ logits,
                                                      const float *__restrict__ bias, int T, int E,
                                                      int k, uint32_t *__restrict__ selected,
                                                      float *__restrict__ weights) {
@@ -185,22 +193,26 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ l
     if (t >= T) return;  // uniform per group
     int sel;
     float w;
-    route_token<LANES, EPL>(logits, bias, t, E, k, r, (int)(threadIdx.x & 63) & ~(LANES - 1),
-                            &sel, &w);
+    route_token<LANES, EPL, LBF16>(logits, bias, t, E, k, r,
+                                   (int)(threadIdx.x & 63) & ~(LANES - 1), &sel, &w);
     if (r < k) {
         selected[(size_t)t * k + r] = (uint32_t)sel;
         weights[(size_t)t * k + r] = w;
     }
 }
 
-hipError_t launch_router(const float *logits, const float *bias, int T, int E, int k,
-                         uint32_t *selected, float *weights, hipStream_t s) {
+hipError_t launch_router(const void *logits, bool logits_bf16, const float *bias, int T, int E,
+                         int k, uint32_t *selected, float *weights, hipStream_t s) {
     // 16 lanes per token while a lane holds at most 16 experts, else 64
 #define MOEQ_ROUTER(L, N)                                                                \
     if (L * N >= E && k <= L) {                                                          \
         dim3 grid((unsigned)(((size_t)T * L + 255) / 256)), block(256);                  \
-        hipLaunchKernelGGL((router_kernel<L, N>), grid, block, 0, s, logits, bias, T, E, k, \
-                           selected, weights);                                          \
+        if (logits_bf16)                                                                 \
+            hipLaunchKernelGGL((router_kernel<L, N, true>), grid, block, 0, s, logits, bias, \
+                               T, E, k, selected, weights);                              \
+        else                                                                             \
+            hipLaunchKernelGGL((router_kernel<L, N, false>), grid, block, 0, s, logits, bias, \
+                               T, E, k, selected, weights);                              \
         return hipGetLastError();                                                        \
     }
     MOEQ_ROUTER(16, 2)
@@ -230,9 +242,9 @@ constexpr int kSmallT = 256, kSmallA = 4096, kSmallE = 256, kSmallK = 16;
 constexpr int kPre = 2;  // source vectors per thread loaded during the routing (E <= 128)
 typedef uint32_t vec4u __attribute__((ext_vector_type(4)));  // kept in registers
 
-template <int EPL>
+template <int EPL, bool LBF16>
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(
-    const uint8_t *__restrict__ x, int row_bytes, const float *__restrict__ logits,
+    const uint8_t *__restrict__ x, int row_bytes, const void *__restrict__ logits,
     const float *__restrict__ bias, int T, int E, int k, uint8_t *__restrict__ values,
     float *__restrict__ weights, uint32_t *__restrict__ selected,
     uint32_t *__restrict__ row_experts, int32_t *__restrict__ offsets,
@@ -274,7 +286,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
     {
         const int t = tid >> 4, r = tid & 15;
         RouteRaw<EPL> raw;
-        route_load<16, EPL>(logits, bias, min(t, T - 1), E, r, raw);
+        route_load<16, EPL, LBF16>(logits, bias, min(t, T - 1), E, r, raw);
 #pragma unroll
         for (int u = 0; u < PRE; ++u) pre[u] = xv[min(gtid + u * gstride, npairs - 1)];
         route_finish(t, r, raw);
@@ -282,7 +294,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
     for (int t0 = 64; t0 < T; t0 += 64) {
         const int t = t0 + (tid >> 4), r = tid & 15;
         RouteRaw<EPL> raw;
-        route_load<16, EPL>(logits, bias, min(t, T - 1), E, r, raw);
+        route_load<16, EPL, LBF16>(logits, bias, min(t, T - 1), E, r, raw);
         route_finish(t, r, raw);
     }
     for (int e = tid; e < E; e += blockDim.x) {
@@ -407,8 +419,9 @@ bool small_dispatch_fits(int T, int E, int k, size_t row_bytes, const void *x, c
            ((uintptr_t)x | (uintptr_t)values) % 16 == 0 && row_bytes < ((size_t)1 << 30);
 }
 
-hipError_t launch_dispatch_small(const void *x, size_t row_bytes, const float *logits,
-                                 const float *bias, int T, int E, int k, void *values,
+hipError_t launch_dispatch_small(const void *x, size_t row_bytes, const void *logits,
+                                 bool logits_bf16, const float *bias, int T, int E, int k,
+                                 void *values,
                                  float *weights, uint32_t *selected, uint32_t *row_experts,
                                  const moeq_route *route, hipStream_t s) {
     const int A = T * k;
@@ -419,11 +432,18 @@ hipError_t launch_dispatch_small(const void *x, size_t row_bytes, const float *l
     const int epl = (E + 15) / 16;
 #define MOEQ_SMALL(N)                                                                          \
     if (epl <= N) {                                                                            \
-        hipLaunchKernelGGL(dispatch_small_kernel<N>, dim3(blocks), dim3(1024), 0, s,          \
-                           (const uint8_t *)x, (int)row_bytes, logits, bias, T, E, k,           \
-                           (uint8_t *)values, weights, selected, row_experts,                  \
-                           route->expert_offsets, route->row_src, route->slot_pos,             \
-                           route->tile_offsets, route->tile_expert);                           \
+        if (logits_bf16)                                                                       \
+            hipLaunchKernelGGL((dispatch_small_kernel<N, true>), dim3(blocks), dim3(1024), 0, s, \
+                               (const uint8_t *)x, (int)row_bytes, logits, bias, T, E, k,       \
+                               (uint8_t *)values, weights, selected, row_experts,              \
+                               route->expert_offsets, route->row_src, route->slot_pos,         \
+                               route->tile_offsets, route->tile_expert);                       \
+        else                                                                                   \
+            hipLaunchKernelGGL((dispatch_small_kernel<N, false>), dim3(blocks), dim3(1024), 0, \
+                               s, (const uint8_t *)x, (int)row_bytes, logits, bias, T, E, k,    \
+                               (uint8_t *)values, weights, selected, row_experts,              \
+                               route->expert_offsets, route->row_src, route->slot_pos,         \
+                               route->tile_offsets, route->tile_expert);                       \
         return hipGetLastError();                                                              \
     }
     MOEQ_SMALL(2)

@@ -56,7 +56,7 @@ moeq_status scratch_on_current_device(void **out) {
 }  // namespace
 
 extern "C" moeq_status moe_dispatch_static(const void *x, moeq_dtype act, int32_t T, int32_t K,
-                                           const float *logits, int32_t E,
+                                           const void *logits, moeq_dtype logit_dtype, int32_t E,
                                            const float *expert_bias, int32_t top_k,
                                            void *values, float *weights, uint32_t *selected,
                                            uint32_t *row_experts, moeq_route *route,
@@ -77,8 +77,8 @@ extern "C" moeq_status moe_dispatch_static(const void *x, moeq_dtype act, int32_
     moeq_route bound;
     if ((st = moeq_route_bind(&bound, ptr, MOEQ_STATIC_ROUTE_BYTES, T, E, top_k)) != MOEQ_OK)
         return st;
-    st = moe_dispatch(x, act, T, K, logits, E, expert_bias, top_k, values, weights, selected,
-                      row_experts, &bound, stream);
+    st = moe_dispatch(x, act, T, K, logits, logit_dtype, E, expert_bias, top_k, values, weights,
+                      selected, row_experts, &bound, stream);
     if (st == MOEQ_OK) *route = bound;
     return st;
 }

@@ -15,7 +15,8 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "csrc", "libmoeq.so")
+# MOEQ_LIB names another build of the same library (the host-sanitized one)
+LIB_PATH = os.environ.get("MOEQ_LIB") or os.path.join(_HERE, "csrc", "libmoeq.so")
 
 OK, EINVAL, ESHAPE, EDTYPE, ERANGE, EWORKSPACE, EUNSUPPORTED, EDEVICE = 0, -1, -2, -3, -4, -5, -6, -7
 F32, F16, BF16 = 0, 1, 2
@@ -83,7 +84,7 @@ def lib():
     L.moeq_route_bind.restype = C.c_int
     L.moeq_route_bind.argtypes = [C.POINTER(Route), vp, C.c_size_t, i32, i32, i32]
     L.moe_dispatch.restype = C.c_int
-    L.moe_dispatch.argtypes = [vp, C.c_int, i32, i32, vp, i32, vp, i32, vp, vp, vp, vp,
+    L.moe_dispatch.argtypes = [vp, C.c_int, i32, i32, vp, C.c_int, i32, vp, i32, vp, vp, vp, vp,
                                C.POINTER(Route), vp]
     L.moe_dispatch_static.restype = C.c_int
     L.moe_dispatch_static.argtypes = L.moe_dispatch.argtypes
@@ -308,9 +309,11 @@ def moe_dispatch(x: torch.Tensor, logits: torch.Tensor, expert_bias: Optional[to
                    weights=torch.empty(T, top_k, dtype=torch.float32, device=x.device),
                    selected=torch.empty(T, top_k, dtype=torch.int32, device=x.device),
                    row_experts=torch.empty(A, dtype=torch.int32, device=x.device))
-    if logits.dtype != torch.float32 or (expert_bias is not None and expert_bias.dtype != torch.float32):
-        raise MoeqError(EDTYPE, "logits and expert bias are fp32")
-    _check(lib().moe_dispatch(_ptr(x), _dt(x), T, K, _ptr(logits), E, _ptr(expert_bias), top_k,
+    if logits.dtype not in (torch.float32, torch.bfloat16) or (
+            expert_bias is not None and expert_bias.dtype != torch.float32):
+        raise MoeqError(EDTYPE, "logits are fp32 or bf16, the expert bias fp32")
+    _check(lib().moe_dispatch(_ptr(x), _dt(x), T, K, _ptr(logits), _dt(logits), E,
+                              _ptr(expert_bias), top_k,
                               _ptr(out["values"]), _ptr(out["weights"]), _ptr(out["selected"]),
                               _ptr(out["row_experts"]), C.byref(route.c), _stream(x.device)))
     out["route"] = route
@@ -344,11 +347,13 @@ def moe_dispatch_static(x: torch.Tensor, logits: torch.Tensor,
                    weights=torch.empty(T, top_k, dtype=torch.float32, device=x.device),
                    selected=torch.empty(T, top_k, dtype=torch.int32, device=x.device),
                    row_experts=torch.empty(A, dtype=torch.int32, device=x.device))
-    if logits.dtype != torch.float32 or (expert_bias is not None and expert_bias.dtype != torch.float32):
-        raise MoeqError(EDTYPE, "logits and expert bias are fp32")
+    if logits.dtype not in (torch.float32, torch.bfloat16) or (
+            expert_bias is not None and expert_bias.dtype != torch.float32):
+        raise MoeqError(EDTYPE, "logits are fp32 or bf16, the expert bias fp32")
     if route is None:
         route = StaticRoute(x.device)
-    _check(lib().moe_dispatch_static(_ptr(x), _dt(x), T, K, _ptr(logits), E, _ptr(expert_bias),
+    _check(lib().moe_dispatch_static(_ptr(x), _dt(x), T, K, _ptr(logits), _dt(logits), E,
+                                     _ptr(expert_bias),
                                      top_k, _ptr(out["values"]), _ptr(out["weights"]),
                                      _ptr(out["selected"]), _ptr(out["row_experts"]),
                                      C.byref(route.c), _stream(x.device)))

@@ -81,9 +81,9 @@ def test_route_bind_errors(L):
     assert bind(L, 4, 8, 9)[0] == moeq.EINVAL
 
 
-def dispatch(L, route, T=4, E=8, k=2, K=16, act=moeq.BF16, ptr=FAKE):
+def dispatch(L, route, T=4, E=8, k=2, K=16, act=moeq.BF16, ptr=FAKE, ldt=moeq.F32):
     p = C.c_void_p(ptr)
-    return L.moe_dispatch(p, act, T, K, p, E, None, k, p, p, p, p, C.byref(route), None)
+    return L.moe_dispatch(p, act, T, K, p, ldt, E, None, k, p, p, p, p, C.byref(route), None)
 
 
 def test_dispatch_validation(L):
@@ -92,6 +92,9 @@ def test_dispatch_validation(L):
     assert dispatch(L, r, T=5) == moeq.ESHAPE
     assert dispatch(L, r, k=3) == moeq.ESHAPE
     assert dispatch(L, r, act=7) == moeq.EDTYPE
+    assert dispatch(L, r, ldt=moeq.F16) == moeq.EDTYPE          # logits: fp32 or bf16
+    assert b"logits" in L.moeq_last_error()
+    assert dispatch(L, r, ldt=9) == moeq.EDTYPE
     assert dispatch(L, r, K=0) == moeq.EINVAL
     assert dispatch(L, r, ptr=0) == moeq.EINVAL                 # NULL tensors
     st, r = bind(L, 4, 4096, 2)

@@ -459,23 +459,27 @@ def test_mxfp4_tiled_path_parity(T, E, k, H, I, edge_scales, kernel, monkeypatch
     assert row_rel_err(y_gpu[keep], yr[keep]) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("sdt,bias,kernel", [("bf16", False, "wave"), ("f32", True, "ws"),
-                                             ("f16", True, "ws")])
-def test_split_path_parity(sdt, bias, kernel, monkeypatch):
+@pytest.mark.parametrize("sdt,bias,kernel,group", [("bf16", False, "wave", 128),
+                                                   ("f32", True, "ws", 128),
+                                                   ("f16", True, "ws", 128),
+                                                   ("bf16", True, "wave", 64),
+                                                   ("f32", False, "ws", 64)])
+def test_split_path_parity(sdt, bias, kernel, group, monkeypatch):
     """Skewed routing at 8 < rows per expert <= 64: experts with at most 32 rows
     run on the weight-streaming kernel, the heavier ones on an m-tile kernel
     (register-decoded, or warp-specialised when it is switched off or the scales
     are fp32), each skipping the other's experts.  Forward stages and the chain
-    input VJP against the oracle."""
+    input VJP against the oracle.  Group 64 takes the streaming kernel's
+    unpipelined two-row-tile form (no split over K)."""
     if kernel == "ws":
         monkeypatch.setenv("MOEQ_WAVE", "0")
     cfg = dataclasses.replace(CONFIGS["decode"], T=384, E=64, k=4, H=512, I=256, sdt=sdt,
-                              awq_bias=bias)
+                              awq_bias=bias, group=group)
     p = make_inputs(cfg, seed=55)
     rb = np.zeros(p["E"], np.float32)
     rb[[3, 17, 40, 41, 63]] = [3.0, 2.5, 2.0, 1.5, 1.0]     # a few heavy experts
     p["router_bias"] = rb
-    print(f"[split] sdt={sdt} bias={bias} kernel={kernel}", flush=True)
+    print(f"[split] sdt={sdt} bias={bias} kernel={kernel} group={group}", flush=True)
     g = run_path(p)
     check_dispatch(p, g)
     rows = np.diff(g["offsets"])
@@ -501,3 +505,29 @@ def test_split_path_parity(sdt, bias, kernel, monkeypatch):
                                           (p["up_qw"], p["up_qz"], p["up_s"], p["up_b"]), sdt,
                                           p["group"], dh)
     assert row_rel_err(f64(di.to_host(gv, "bf16"), "bf16"), f64(rv, "bf16")) <= tol
+
+
+@pytest.mark.parametrize("name,T,E,k", [("decode", 64, 128, 8), ("prefill", 1000, 128, 8),
+                                        ("many", 200, 512, 10), ("decode", 64, 256, 16)])
+def test_router_bf16_logits(name, T, E, k):
+    """bf16 router logits (a logit dtype the boundary takes): widened exactly to
+    fp32, then routed as fp32 logits are.  bf16 values repeat often, so ties are
+    frequent; selection, weights and the dispatch order match the oracle on the
+    widened values bit for bit (weights to one fp32 rounding)."""
+    cfg = dataclasses.replace(CONFIGS[name], T=T, E=E, k=k)
+    p = make_inputs(cfg, seed=71)
+    lb = to_storage(np.random.default_rng(72).normal(0, 1, (T, E)), "bf16")
+    p["logits"] = (lb.astype(np.uint32) << 16).view(np.float32)    # the exact widening
+    print(f"[bf16 logits] {name} T={T} E={E} k={k}", flush=True)
+    d = di.upload(p, DEV)
+    disp = moeq.moe_dispatch(d["x"], di.tensor(lb, "bf16", DEV), d["router_bias"], k)
+    torch.cuda.synchronize()
+    r = disp["route"]
+    g = dict(selected=disp["selected"].cpu().numpy().view(np.uint32),
+             weights=disp["weights"].cpu().numpy(),
+             row_experts=disp["row_experts"].cpu().numpy().view(np.uint32),
+             values=di.to_host(disp["values"], p["adt"]), offsets=r.expert_offsets.cpu().numpy(),
+             row_src=r.row_src.cpu().numpy(), slot_pos=r.slot_pos.cpu().numpy())
+    check_dispatch(p, g)
+    # ties occur: some token has equal widened scores among its candidates
+    assert any(len(np.unique(row)) < E for row in p["logits"])

@@ -81,13 +81,13 @@ def test_static_dispatch_limit_and_failure_leave_route():
     need = moeq.lib().moeq_route_workspace_bytes(T, 512, 10)
     assert need > (4 << 20)
     L, r = moeq.lib(), disp["route"]
-    st = L.moe_dispatch_static(None, moeq.BF16, T, 256, None, 512, None, 10, None, None, None,
-                               None, C.byref(r.c), None)
+    st = L.moe_dispatch_static(None, moeq.BF16, T, 256, None, moeq.F32, 512, None, 10, None,
+                               None, None, None, C.byref(r.c), None)
     assert st == moeq.EWORKSPACE and b"static route array" in L.moeq_last_error()
     # invalid arguments: nothing enqueued, route untouched
     st = L.moe_dispatch_static(C.c_void_p(x.data_ptr()), 7, 64, 256,
-                               C.c_void_p(logits.data_ptr()), 128, None, 8, None, None, None,
-                               None, C.byref(r.c), None)
+                               C.c_void_p(logits.data_ptr()), moeq.F32, 128, None, 8, None, None,
+                               None, None, C.byref(r.c), None)
     assert st == moeq.EDTYPE
     assert bytes(r.c) == before
     torch.cuda.synchronize()
