@@ -74,11 +74,11 @@ moeq_status report_error(moeq_status st, const char *fmt, ...);
 
 hipError_t launch_router(const void *logits, bool logits_bf16, const float *bias, int T, int E,
                          int k, uint32_t *selected, float *weights, hipStream_t s);
-bool small_dispatch_fits(int T, int E, int k, size_t row_bytes, const void *x, const void *values);
-hipError_t launch_dispatch_small(const void *x, size_t row_bytes, const void *logits,
-                                 bool logits_bf16, const float *bias, int T, int E, int k,
-                                 void *values, float *weights, uint32_t *selected, uint32_t *row_experts,
-                                 const moeq_route *route, hipStream_t s);
+bool index_rows_fits(int T, int E, int k, size_t row_bytes, const void *x, const void *values);
+// after launch_router: the stable order, the route and the row copies in one launch
+hipError_t launch_index_rows(const void *x, size_t row_bytes, const uint32_t *selected, int T,
+                             int E, int k, void *values, uint32_t *row_experts,
+                             const moeq_route *route, hipStream_t s);
 hipError_t launch_dispatch_index(const uint32_t *selected, int T, int E, int k,
                                  const moeq_route *route, uint32_t *row_experts,
                                  hipStream_t s);

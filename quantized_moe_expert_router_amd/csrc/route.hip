@@ -225,232 +225,192 @@ hipError_t launch_router(const void *logits, bool logits_bf16, const float *bias
     return hipErrorInvalidValue;
 }
 
-// ------------------------------------------------------------------ fused small dispatch
-// Whole dispatch in one launch for small batches (T <= 256, T*k <= 4096,
-// E <= 256, top_k <= 16).  Every block routes all T tokens into LDS (the
-// logits are a few tens of KB, L2-resident), builds the stable order there --
-// expert histogram, exclusive scan, and the rank of token t among the tokens
-// of expert e as a popcount over a per-expert token bitmask -- then block 0
-// writes the routing outputs and every block copies its share of rows.
+// ------------------------------------------------------------------ two-launch dispatch
+// Dispatch in two launches while the per-expert token bitmasks fit in LDS
+// (E * ceil(T/64) <= 8192 words, T <= 4096): the router kernel, then
+// index_rows_kernel.  Block b of the latter owns tokens [b*tpb, (b+1)*tpb).  It
+// reads all T*k selections (L2-resident), sets bit t of word t/64 of expert e's
+// mask for each, counts each expert's rows from the masks and scans them with
+// one wave (no block-wide barrier inside the scan).  The rank of its own
+// assignment (t, e) among expert e's rows is then the popcount of the mask
+// words below t, one wave per assignment; the block writes the route entries of
+// its own tokens (block 0 also the offsets and m-tile lists) and copies their
+// rows.  The index work is repeated in every block, but it is a few us of LDS
+// traffic, and it replaces three launches of the multi-pass path below.
+// (Routing in that same launch, as one earlier design did for small batches,
+// kept each CU's VALU busy for about 5 us at decode: every block would route
+// every token.)
 //
 // The copy runs over source vectors: x is [T][vecs] 16-byte vectors, and
 // vector (t, i) goes to row slot_pos[t, j] of every slot j.  A thread's first
-// kPre vectors are loaded right behind the first routing pass's logits, so
-// their latency overlaps the routing, and stored once the positions are known
-// (not for E > 128, whose routing already fills the registers).
-constexpr int kSmallT = 256, kSmallA = 4096, kSmallE = 256, kSmallK = 16;
-constexpr int kPre = 2;  // source vectors per thread loaded during the routing (E <= 128)
+// kIdxPre vectors are loaded before the selections, so their latency overlaps
+// the index work.
+constexpr int kIdxWords = 8192;      // mask words in LDS (64 KB)
+constexpr int kIdxMaxTokens = 16;    // tokens owned per block: T <= 256 * 16
+constexpr int kIdxThreads = 1024;
+constexpr int kIdxPre = 4;
+constexpr int kIdxMaxAssign = 16384;  // T * k
 typedef uint32_t vec4u __attribute__((ext_vector_type(4)));  // kept in registers
 
-template <int EPL, bool LBF16>
-__global__ __launch_bounds__(1024) void dispatch_small_kernel(
-    const uint8_t *__restrict__ x, int row_bytes, const void *__restrict__ logits,
-    const float *__restrict__ bias, int T, int E, int k, uint8_t *__restrict__ values,
-    float *__restrict__ weights, uint32_t *__restrict__ selected,
-    uint32_t *__restrict__ row_experts, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ row_src_g, int32_t *__restrict__ slot_pos_g,
-    int32_t *__restrict__ tile_offsets_g, int32_t *__restrict__ tile_expert_g) {
-    __shared__ uint16_t sel_s[kSmallA];
-    __shared__ float w_s[kSmallA];
-    __shared__ int32_t pos_s[kSmallA];
-    __shared__ int32_t hist_s[kSmallE];
-    __shared__ int32_t off_s[kSmallE + 1];
-    __shared__ unsigned long long mask_s[kSmallE][kSmallT / 64];
-    __shared__ int wave_tot[16];
-    const int tid = threadIdx.x, A = T * k;
-    const int MW = (T + 63) / 64;
+// Exclusive scans over experts by one wave (lane l owns a contiguous run of
+// experts): rows (off_s, offsets), m-tiles of the tiled projections
+// (tile_offsets, tile_expert) and their scheduling order (tile_order: every
+// full m-tile in m-tile order, then the partial ones).
+__device__ void scan_experts_wave(const int32_t *hist_s, int E, int A, bool write_route,
+                                  int32_t *off_s, int32_t *__restrict__ offsets,
+                                  int32_t *__restrict__ tile_offsets,
+                                  int32_t *__restrict__ tile_expert,
+                                  int32_t *__restrict__ tile_order) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int per = (E + kWave - 1) / kWave;
+    const int e0 = min(lane * per, E), e1 = min(e0 + per, E);
+    int sc = 0, st = 0, sf = 0, sp = 0;
+    for (int e = e0; e < e1; ++e) {
+        const int c = hist_s[e], nt = (c + kTileRows - 1) / kTileRows, nf = c / kTileRows;
+        sc += c;
+        st += nt;
+        sf += nf;
+        sp += nt - nf;
+    }
+    int ic = sc, it = st, iff = sf, ip = sp;  // inclusive over lanes
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int a0 = __shfl_up(ic, o), a1 = __shfl_up(it, o);
+        const int a2 = __shfl_up(iff, o), a3 = __shfl_up(ip, o);
+        if (lane >= o) {
+            ic += a0;
+            it += a1;
+            iff += a2;
+            ip += a3;
+        }
+    }
+    const int ftotal = __shfl(iff, kWave - 1);
+    int ec = ic - sc, et = it - st, ef = iff - sf, ep = ip - sp;
+    for (int e = e0; e < e1; ++e) {
+        const int c = hist_s[e], nt = (c + kTileRows - 1) / kTileRows, nf = c / kTileRows;
+        off_s[e] = ec;
+        if (write_route) {
+            offsets[e] = ec;
+            tile_offsets[e] = et;
+            for (int t = 0; t < nt; ++t) tile_expert[et + t] = e;
+            for (int t = 0; t < nf; ++t) tile_order[ef + t] = et + t;
+            if (nt > nf) tile_order[ftotal + ep] = et + nf;
+        }
+        ec += c;
+        et += nt;
+        ef += nf;
+        ep += nt - nf;
+    }
+    if (lane == kWave - 1) {
+        off_s[E] = A;
+        if (write_route) {
+            offsets[E] = A;
+            tile_offsets[E] = it;
+        }
+    }
+}
 
-    const int vecs = row_bytes / 16;
-    const long npairs = (long)T * vecs;  // source vectors
-    const long gtid = (long)blockIdx.x * blockDim.x + tid, gstride = (long)gridDim.x * blockDim.x;
-    const vec4u *__restrict__ xv = reinterpret_cast<const vec4u *>(x);
-    constexpr int PRE = EPL <= 8 ? kPre : 0;
-    vec4u pre[PRE > 0 ? PRE : 1];
+__global__ __launch_bounds__(kIdxThreads) void index_rows_kernel(
+    const vec4u *__restrict__ x, int vecs, const uint32_t *__restrict__ selected, int T, int E,
+    int k, int tpb, vec4u *__restrict__ values, uint32_t *__restrict__ row_experts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ row_src, int32_t *__restrict__ slot_pos,
+    int32_t *__restrict__ tile_offsets, int32_t *__restrict__ tile_expert) {
+    __shared__ unsigned long long mask_s[kIdxWords];
+    __shared__ int32_t hist_s[kMaxExperts];
+    __shared__ int32_t off_s[kMaxExperts + 1];
+    __shared__ int32_t pos_s[kIdxMaxTokens * kMaxTopK];
+    const int tid = threadIdx.x, A = T * k, MW = (T + 63) / 64;
+    const int t0 = blockIdx.x * tpb, t1 = min(t0 + tpb, T);
+    const long v0 = (long)t0 * vecs, nv = (long)(t1 - t0) * vecs;
+    vec4u pre[kIdxPre];
+#pragma unroll
+    for (int u = 0; u < kIdxPre; ++u) pre[u] = x[v0 + min((long)u * kIdxThreads + tid, nv - 1)];
 
-    // 1. routing: 64 rows of 16 lanes per pass (loads at a clamped token, so
-    //    no load sits in a branch); the first pass also issues the prefetch
-    auto route_finish = [&](int t, int r, const RouteRaw<EPL> &raw) {
-        if (t < T) {
-            int sel;
-            float w;
-            // 16 keys per lane (E > 128) stay unsorted: the sort would spill at
-            // 1024 threads per block
-            route_select<16, EPL, (EPL <= 8)>(raw, bias != nullptr, E, k, r, (tid & 63) & ~15,
-                                             &sel, &w);
-            if (r < k) {
-                sel_s[t * k + r] = (uint16_t)sel;
-                w_s[t * k + r] = w;
-            }
-        }
-    };
-    {
-        const int t = tid >> 4, r = tid & 15;
-        RouteRaw<EPL> raw;
-        route_load<16, EPL, LBF16>(logits, bias, min(t, T - 1), E, r, raw);
-#pragma unroll
-        for (int u = 0; u < PRE; ++u) pre[u] = xv[min(gtid + u * gstride, npairs - 1)];
-        route_finish(t, r, raw);
-    }
-    for (int t0 = 64; t0 < T; t0 += 64) {
-        const int t = t0 + (tid >> 4), r = tid & 15;
-        RouteRaw<EPL> raw;
-        route_load<16, EPL, LBF16>(logits, bias, min(t, T - 1), E, r, raw);
-        route_finish(t, r, raw);
-    }
-    for (int e = tid; e < E; e += blockDim.x) {
-        hist_s[e] = 0;
-        for (int mw = 0; mw < MW; ++mw) mask_s[e][mw] = 0ull;
+    for (int i = tid; i < E * MW; i += kIdxThreads) mask_s[i] = 0ull;
+    for (int e = tid; e < E; e += kIdxThreads) hist_s[e] = 0;
+    __syncthreads();
+    // 1. per-expert token bitmasks (a token selects an expert at most once)
+    for (int a = tid; a < A; a += kIdxThreads) {
+        const int e = (int)selected[a], t = a / k;
+        atomicOr(&mask_s[e * MW + (t >> 6)], 1ull << (t & 63));
     }
     __syncthreads();
-    // 2. histogram and token bitmask per expert
-    for (int a = tid; a < A; a += blockDim.x) {
-        const int e = sel_s[a], t = a / k;
-        atomicAdd(&hist_s[e], 1);
-        atomicOr(&mask_s[e][t >> 6], 1ull << (t & 63));
+    // 2. rows per expert, then the scans
+    for (int i = tid; i < E * MW; i += kIdxThreads) {
+        const int c = __popcll(mask_s[i]);
+        if (c) atomicAdd(&hist_s[i / MW], c);
     }
     __syncthreads();
-    // 3. exclusive scan of the histogram (E <= 256 < threads: one element each)
-    {
-        const int lane = tid & 63, wv = tid >> 6;
-        const int v = tid < E ? hist_s[tid] : 0;
-        int incl = v;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int n = __shfl_up(incl, o);
-            if (lane >= o) incl += n;
-        }
-        if (lane == kWave - 1) wave_tot[wv] = incl;
-        __syncthreads();
-        int base = 0;
-        for (int w = 0; w < wv; ++w) base += wave_tot[w];
-        if (tid < E) off_s[tid] = base + incl - v;
-        if (tid == 0) off_s[E] = A;
-        // m-tile prefix (tiled projections), written by block 0
-        __syncthreads();
-        const int nt = (v + kTileRows - 1) / kTileRows;
-        int tincl = nt;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int n = __shfl_up(tincl, o);
-            if (lane >= o) tincl += n;
-        }
-        if (lane == kWave - 1) wave_tot[wv] = tincl;
-        __syncthreads();
-        int tbase = 0;
-        for (int w = 0; w < wv; ++w) tbase += wave_tot[w];
-        // scheduling order: every full m-tile (m-tile order), then the partial ones
-        const int nfull = v / kTileRows, npart = nt - nfull;
-        __syncthreads();
-        int fincl = nfull;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int n = __shfl_up(fincl, o);
-            if (lane >= o) fincl += n;
-        }
-        if (lane == kWave - 1) wave_tot[wv] = fincl;
-        __syncthreads();
-        int fbase = 0, ftotal = 0;
-        for (int w = 0; w < wv; ++w) fbase += wave_tot[w];
-        for (int w = 0; w < 16; ++w) ftotal += wave_tot[w];
-        __syncthreads();
-        int pincl = npart;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int n = __shfl_up(pincl, o);
-            if (lane >= o) pincl += n;
-        }
-        if (lane == kWave - 1) wave_tot[wv] = pincl;
-        __syncthreads();
-        int pbase = 0;
-        for (int w = 0; w < wv; ++w) pbase += wave_tot[w];
-        if (blockIdx.x == 0) {
-            int32_t *tile_order_g = tile_expert_g + tile_cap(A, E);
-            if (tid < E) {
-                const int first = tbase + tincl - nt;
-                tile_offsets_g[tid] = first;
-                for (int t = 0; t < nt; ++t) tile_expert_g[first + t] = tid;
-                const int fpos = fbase + fincl - nfull;
-                for (int t = 0; t < nfull; ++t) tile_order_g[fpos + t] = first + t;
-                if (npart) tile_order_g[ftotal + pbase + pincl - 1] = first + nfull;
-            }
-            if (tid == E - 1) tile_offsets_g[E] = tbase + tincl;
-        }
-    }
+    if (tid < kWave)
+        scan_experts_wave(hist_s, E, A, blockIdx.x == 0, off_s, offsets, tile_offsets,
+                          tile_expert, tile_expert + tile_cap(A, E));
     __syncthreads();
-    // 4. stable positions: rank of token t among the tokens of expert e
-    for (int a = tid; a < A; a += blockDim.x) {
-        const int e = sel_s[a], t = a / k;
-        int rank = __popcll(mask_s[e][t >> 6] & ((1ull << (t & 63)) - 1ull));
-        for (int mw = 0; mw < (t >> 6); ++mw) rank += __popcll(mask_s[e][mw]);
-        const int p = off_s[e] + rank;
-        pos_s[a] = p;
-        if (blockIdx.x == 0) {
-            slot_pos_g[a] = p;
-            row_src_g[p] = t;
+    // 3. stable positions of the block's own assignments: the rank of token t
+    //    among the tokens of expert e, one wave per assignment
+    const int wv = tid / kWave, lane = tid & (kWave - 1);
+    const int na = (t1 - t0) * k;
+    for (int q = wv; q < na; q += kIdxThreads / kWave) {
+        const int a = t0 * k + q, t = a / k;
+        const int e = (int)selected[a];
+        const int tw = t >> 6;
+        int c = 0;
+        if (lane < tw)
+            c = __popcll(mask_s[e * MW + lane]);
+        else if (lane == tw)
+            c = __popcll(mask_s[e * MW + lane] & ((1ull << (t & 63)) - 1ull));
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) c += __shfl_xor(c, o);
+        if (lane == 0) {
+            const int p = off_s[e] + c;
+            pos_s[q] = p;
+            slot_pos[a] = p;
+            row_src[p] = t;
             row_experts[p] = (uint32_t)e;
-            selected[a] = (uint32_t)e;
-            weights[a] = w_s[a];
         }
     }
-    if (blockIdx.x == 0)
-        for (int e = tid; e <= E; e += blockDim.x) offsets[e] = off_s[e];
     __syncthreads();
-    // 5. row copies: each source vector is stored to the rows of the token's k
+    // 4. row copies: each source vector is stored to the rows of the token's k
     //    slots (for a fixed slot, consecutive threads write consecutive vectors)
-    vec4u *__restrict__ vv = reinterpret_cast<vec4u *>(values);
 #pragma unroll
-    for (int u = 0; u < PRE; ++u) {
-        const long pr = gtid + u * gstride;
-        if (pr < npairs) {
-            const int t = (int)(pr / vecs), i = (int)(pr - (long)t * vecs);
-            for (int j = 0; j < k; ++j) vv[(size_t)pos_s[t * k + j] * vecs + i] = pre[u];
+    for (int u = 0; u < kIdxPre; ++u) {
+        const long pr = (long)u * kIdxThreads + tid;
+        if (pr < nv) {
+            const int tl = (int)(pr / vecs), i = (int)(pr - (long)tl * vecs);
+            for (int j = 0; j < k; ++j) values[(size_t)pos_s[tl * k + j] * vecs + i] = pre[u];
         }
     }
-    for (long pr = gtid + PRE * gstride; pr < npairs; pr += gstride) {
-        const vec4u v = xv[pr];
-        const int t = (int)(pr / vecs), i = (int)(pr - (long)t * vecs);
-        for (int j = 0; j < k; ++j) vv[(size_t)pos_s[t * k + j] * vecs + i] = v;
+    for (long pr = (long)kIdxPre * kIdxThreads + tid; pr < nv; pr += kIdxThreads) {
+        const vec4u v = x[v0 + pr];
+        const int tl = (int)(pr / vecs), i = (int)(pr - (long)tl * vecs);
+        for (int j = 0; j < k; ++j) values[(size_t)pos_s[tl * k + j] * vecs + i] = v;
     }
 }
 
-bool small_dispatch_fits(int T, int E, int k, size_t row_bytes, const void *x, const void *values) {
-    return T >= 1 && T <= kSmallT && T * k <= kSmallA && E <= kSmallE && k <= kSmallK &&
-           row_bytes >= 16 && row_bytes % 16 == 0 &&
-           ((uintptr_t)x | (uintptr_t)values) % 16 == 0 && row_bytes < ((size_t)1 << 30);
+int index_rows_tpb(int T) { return T <= 256 ? 1 : (T + 255) / 256; }
+
+bool index_rows_fits(int T, int E, int k, size_t row_bytes, const void *x, const void *values) {
+    if (T < 1 || T > 256 * kIdxMaxTokens || E < 1 || E > kMaxExperts || k < 1 || k > kMaxTopK)
+        return false;
+    if ((long)E * ((T + 63) / 64) > kIdxWords) return false;
+    // every block reads all T*k selections: at prefill size (32768) that and the
+    // copy of 16 tokens per block, one block per CU, took 55 us against 46 us for
+    // the multi-pass path
+    if ((long)T * k > kIdxMaxAssign) return false;
+    if (index_rows_tpb(T) * k > kIdxMaxTokens * kMaxTopK) return false;
+    return row_bytes >= 16 && row_bytes % 16 == 0 && row_bytes < ((size_t)1 << 30) &&
+           ((uintptr_t)x | (uintptr_t)values) % 16 == 0;
 }
 
-hipError_t launch_dispatch_small(const void *x, size_t row_bytes, const void *logits,
-                                 bool logits_bf16, const float *bias, int T, int E, int k,
-                                 void *values,
-                                 float *weights, uint32_t *selected, uint32_t *row_experts,
-                                 const moeq_route *route, hipStream_t s) {
-    const int A = T * k;
-    // enough blocks that every thread copies four 16-byte vectors (at most 256)
-    const long vecs = (long)A * (long)(row_bytes / 16);
-    long want = (vecs + 1024 * 4 - 1) / (1024 * 4);
-    const int blocks = (int)(want < 1 ? 1 : (want > 256 ? 256 : want));
-    const int epl = (E + 15) / 16;
-#define MOEQ_SMALL(N)                                                                          \
-    if (epl <= N) {                                                                            \
-        if (logits_bf16)                                                                       \
-            hipLaunchKernelGGL((dispatch_small_kernel<N, true>), dim3(blocks), dim3(1024), 0, s, \
-                               (const uint8_t *)x, (int)row_bytes, logits, bias, T, E, k,       \
-                               (uint8_t *)values, weights, selected, row_experts,              \
-                               route->expert_offsets, route->row_src, route->slot_pos,         \
-                               route->tile_offsets, route->tile_expert);                       \
-        else                                                                                   \
-            hipLaunchKernelGGL((dispatch_small_kernel<N, false>), dim3(blocks), dim3(1024), 0, \
-                               s, (const uint8_t *)x, (int)row_bytes, logits, bias, T, E, k,    \
-                               (uint8_t *)values, weights, selected, row_experts,              \
-                               route->expert_offsets, route->row_src, route->slot_pos,         \
-                               route->tile_offsets, route->tile_expert);                       \
-        return hipGetLastError();                                                              \
-    }
-    MOEQ_SMALL(2)
-    MOEQ_SMALL(8)
-    MOEQ_SMALL(16)
-#undef MOEQ_SMALL
-    return hipErrorInvalidValue;
+hipError_t launch_index_rows(const void *x, size_t row_bytes, const uint32_t *selected, int T,
+                             int E, int k, void *values, uint32_t *row_experts,
+                             const moeq_route *route, hipStream_t s) {
+    const int tpb = index_rows_tpb(T);
+    const int blocks = (T + tpb - 1) / tpb;
+    hipLaunchKernelGGL(index_rows_kernel, dim3(blocks), dim3(kIdxThreads), 0, s,
+                       (const vec4u *)x, (int)(row_bytes / 16), selected, T, E, k, tpb,
+                       (vec4u *)values, row_experts, route->expert_offsets, route->row_src,
+                       route->slot_pos, route->tile_offsets, route->tile_expert);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ dispatch

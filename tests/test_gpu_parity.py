@@ -209,14 +209,21 @@ def test_dispatch_over_128_experts(T, E, k):
 
 
 @pytest.mark.parametrize("T,E,k,K,adt", [
-    (301, 64, 32, 128, "bf16"),   # 256-byte rows: 16 vectors, blocks aligned to 64 tokens, k at the limit
-    (300, 128, 8, 136, "bf16"),   # 272-byte rows: blocks straddle tokens
-    (300, 128, 4, 120, "bf16"),   # 240-byte rows: below the scatter's minimum, row-copy kernel
+    # two-launch dispatch (token bitmasks in LDS)
+    (301, 64, 32, 128, "bf16"),   # 256-byte rows, k at the limit, two tokens per block
+    (300, 128, 8, 136, "bf16"),   # 272-byte rows
+    (300, 128, 4, 120, "bf16"),   # 240-byte rows
     (257, 32, 6, 64, "f32"),      # 256-byte fp32 rows
+    (4096, 2, 1, 8, "bf16"),      # 16-byte rows, 16 tokens per block, 64 mask words per expert
+    # multi-pass dispatch (T > 4096): source-major scatter, then the row-copy kernel
+    (4161, 128, 4, 136, "bf16"),  # 272-byte rows: scatter blocks straddle tokens
+    (4161, 64, 2, 120, "bf16"),   # 240-byte rows: below the scatter's minimum, row-copy kernel
 ])
 def test_dispatch_row_scatter_edges(T, E, k, K, adt):
-    """Large-batch COPY at the edges of the source-major scatter (rows of at least
-    16 vectors; its LDS holds the slot positions of at most 65 tokens)."""
+    """COPY at the edges of both dispatch paths: the two-launch one (every block
+    owns up to 16 tokens and ranks them from per-expert token bitmasks) and the
+    multi-pass one for larger batches (its source-major scatter needs rows of at
+    least 16 vectors and holds the slot positions of at most 65 tokens)."""
     rng = np.random.default_rng(T + 3 * E + k + K)
     logits = rng.normal(0, 1, (T, E)).astype(np.float32)
     x = to_storage(rng.normal(0, 1, (T, K)), adt)

@@ -59,30 +59,33 @@ def _clang_runtime():
     return hits[-1]
 
 
+def _instrumented(lib):
+    syms = subprocess.run(["nm", "-u", lib], capture_output=True, text=True).stdout
+    assert "__asan_report_load" in syms, lib
+    assert "__ubsan_handle_" in syms, lib
+
+
 def test_oracle_under_sanitizers():
     runtime = _gcc_runtime()
     from oracle import build as ob
-    ob.build(sanitize=True)
-    out = _run(ORACLE_TESTS, {"LD_PRELOAD": runtime, "MOEQ_ORACLE_SANITIZE": "1"})
-    assert "failed" not in out
+    lib = ob.build(sanitize=True)
+    try:
+        _instrumented(lib)
+        out = _run(ORACLE_TESTS, {"LD_PRELOAD": runtime, "MOEQ_ORACLE_SANITIZE": "1"})
+        assert "failed" not in out
+    finally:
+        os.remove(lib)
 
 
 def test_host_validation_under_sanitizers():
+    """The library built this way is as large as the product library and only
+    serves this test, so it is removed afterwards."""
     runtime = _clang_runtime()
     from quantized_moe_expert_router_amd import build as pb
     lib = pb.build_host_sanitized()
-    out = _run(HOST_TESTS, {"LD_PRELOAD": runtime, "MOEQ_LIB": lib})
-    assert "failed" not in out
-
-
-def test_sanitized_libraries_are_instrumented():
-    """The legs above test instrumented code: both libraries call the sanitizer
-    runtimes, and the binding and the oracle load them when asked."""
-    from oracle import build as ob
-    from quantized_moe_expert_router_amd import build as pb
-    for lib in (ob.SAN_LIB, pb.HOSTSAN_LIB):
-        if not os.path.exists(lib):
-            pytest.skip(f"{os.path.basename(lib)} is built by the legs above")
-        syms = subprocess.run(["nm", "-u", lib], capture_output=True, text=True).stdout
-        assert "__asan_report_load" in syms, lib
-        assert "__ubsan_handle_" in syms, lib
+    try:
+        _instrumented(lib)
+        out = _run(HOST_TESTS, {"LD_PRELOAD": runtime, "MOEQ_LIB": lib})
+        assert "failed" not in out
+    finally:
+        os.remove(lib)
