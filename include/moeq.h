@@ -46,6 +46,10 @@
  *    returns MOEQ_EUNSUPPORTED.
  *  - Calls on one stream are ordered; calls that share output buffers on
  *    different streams race.
+ *  - Activation and gradient storage (`act`, `gdt`) is F32, F16 or BF16 unless a
+ *    call says otherwise (frozen_awq.rs: the input storage may differ from the
+ *    scales').  The MFMA kernels take BF16 rows; F32 and F16 rows run on the
+ *    fp32 VALU kernels with the same rounding points.
  */
 #ifndef MOEQ_H
 #define MOEQ_H
@@ -168,7 +172,7 @@ typedef struct moeq_swiglu {
 
 /*
  * moe_dispatch -- moe_exchange.rs MoeDispatchOps::moe_dispatch / MoeDispatched.
- *   x        [T, K] act (F32 or BF16)          input rows
+ *   x        [T, K] act (F32, F16 or BF16)     input rows
  *   logits   [T, E] logit_dtype (F32 or BF16)   router logits; bf16 logits are
  *                                               widened exactly to fp32 first
  *   expert_bias [E] fp32 or NULL                added to the logits (one fp32
@@ -265,7 +269,7 @@ moeq_status moe_combine(const moeq_route *route, const void *y, moeq_dtype act,
  * and packed_experts.rs packed_expert_input_backward: the transpose of the
  * same rounded packed coefficients, no weight / scale / bias gradients:
  *   grad_in[p, :] = round_gdt( grad[p, :] . W_e^T )
- *   grad [rows, N] gdt, grad_in [rows, K] gdt (gdt F32 or BF16).
+ *   grad [rows, N] gdt, grad_in [rows, K] gdt.
  * route != NULL: rows must equal the route's A and row p uses the expert of
  * sorted row p.  route == NULL: the single frozen projection; w must hold one
  * expert and every row uses it.  AWQ only.
@@ -375,7 +379,7 @@ moeq_status awq_expert_forward(const void *x, moeq_dtype act, int32_t rows,
  * packed_expert_input_backward for awq_expert_forward: the transpose of the same
  * rounded coefficients, rows in the incoming order:
  *   grad_in[t, :] = round_gdt( grad[t, :] . W_{id[t]}^T )
- *   grad [rows, N] gdt, grad_in [rows, K] gdt (F32 or BF16); AWQ only.
+ *   grad [rows, N] gdt, grad_in [rows, K] gdt; AWQ only.
  * Same IDs, validation, synchronisation and workspace as awq_expert_forward.
  */
 moeq_status awq_expert_input_backward(const void *grad, moeq_dtype gdt, int32_t rows,

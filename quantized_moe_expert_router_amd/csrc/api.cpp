@@ -360,7 +360,6 @@ moeq_status awq_grouped_swiglu(const moeq_route *route, const void *values, moeq
             return fail(MOEQ_EINVAL, "gate and up must both have or both lack a bias");
         I = gate->out_features;
     }
-    if (act == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 activations are not implemented");
     if (!(fn.clamp >= 0.0f) || !(fn.alpha == fn.alpha) || !(fn.up_offset == fn.up_offset) ||
         (fn.gate_one_sided != 0 && fn.gate_one_sided != 1))
         return fail(MOEQ_EINVAL, "bad SwiGLU parameters");
@@ -399,7 +398,6 @@ moeq_status awq_grouped_down(const moeq_route *route, const void *h, moeq_dtype 
     if (st != MOEQ_OK) return st;
     if (!valid_dtype(act)) return fail(MOEQ_EDTYPE, "unknown activation dtype %d", (int)act);
     if ((st = check_experts(down, "down", route->E, -1, -1, false)) != MOEQ_OK) return st;
-    if (act == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 activations are not implemented");
     const int A = route->T * route->top_k;
     if (A == 0) return MOEQ_OK;
     if (!h || !y) return fail(MOEQ_EINVAL, "NULL tensor pointer");
@@ -459,7 +457,6 @@ moeq_status awq_input_backward(const moeq_route *route, const void *grad, moeq_d
     if (w->format != MOEQ_FMT_AWQ)
         return fail(MOEQ_EUNSUPPORTED, "input VJP is implemented for AWQ cubes");
     if (!valid_dtype(gdt)) return fail(MOEQ_EDTYPE, "unknown gradient dtype %d", (int)gdt);
-    if (gdt == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 gradients are not implemented");
     if (rows == 0) return MOEQ_OK;
     if (!grad || !grad_in) return fail(MOEQ_EINVAL, "NULL tensor pointer");
     ProjProblem p{};
@@ -561,7 +558,6 @@ moeq_status awq_swiglu_input_backward(const moeq_route *route, const void *value
         return fail(MOEQ_EDTYPE, "gate and up must share scale dtype and group size");
     if ((up->bias == nullptr) != (gate->bias == nullptr))
         return fail(MOEQ_EINVAL, "gate and up must both have or both lack a bias");
-    if (act == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 activations are not implemented");
     if (!(fn.clamp >= 0.0f) || !(fn.alpha == fn.alpha) || !(fn.up_offset == fn.up_offset) ||
         (fn.gate_one_sided != 0 && fn.gate_one_sided != 1))
         return fail(MOEQ_EINVAL, "bad SwiGLU parameters");
@@ -819,7 +815,6 @@ moeq_status awq_expert_forward(const void *x, moeq_dtype act, int32_t rows,
     if ((st = check_experts(w, "weights", -1, -1, -1, false)) != MOEQ_OK) return st;
     if (w->experts > kMaxExperts)
         return fail(MOEQ_EUNSUPPORTED, "the local sort implements up to %d experts", kMaxExperts);
-    if (act == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 activations are not implemented");
     const int K = w->in_features, N = w->out_features;
     if (rows == 0) return MOEQ_OK;
     if (!y) return fail(MOEQ_EINVAL, "NULL tensor pointer");
@@ -866,7 +861,6 @@ moeq_status awq_expert_input_backward(const void *grad, moeq_dtype gdt, int32_t 
         return fail(MOEQ_EUNSUPPORTED, "input VJP is implemented for AWQ cubes");
     if (w->experts > kMaxExperts)
         return fail(MOEQ_EUNSUPPORTED, "the local sort implements up to %d experts", kMaxExperts);
-    if (gdt == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 gradients are not implemented");
     const int K = w->in_features, N = w->out_features;
     if (rows == 0) return MOEQ_OK;
     if (!grad_in) return fail(MOEQ_EINVAL, "NULL tensor pointer");
@@ -916,7 +910,6 @@ moeq_status frozen_awq_forward(const void *x, moeq_dtype act, int32_t rows,
     if (w->experts != 1)
         return fail(MOEQ_ERANGE, "a single frozen projection holds one expert, has %d",
                     w->experts);
-    if (act == MOEQ_F16) return fail(MOEQ_EUNSUPPORTED, "fp16 activations are not implemented");
     if (rows == 0) return MOEQ_OK;
     if (!x || !y) return fail(MOEQ_EINVAL, "NULL tensor pointer");
     const size_t need = frozen_awq_workspace_bytes(rows);

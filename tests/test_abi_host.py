@@ -152,7 +152,7 @@ def test_projection_validation(L):
     assert swiglu(L, r, awq(qz=None), awq()) == moeq.EINVAL
     assert swiglu(L, r, awq(), awq(bias=FAKE)) == moeq.EINVAL
     assert swiglu(L, r, awq(), None) == moeq.EINVAL
-    assert swiglu(L, r, awq(), awq(), act=moeq.F16) == moeq.EUNSUPPORTED
+    assert swiglu(L, r, awq(), awq(), act=moeq.F16) == moeq.OK   # fp16 rows: VALU kernels
     assert swiglu(L, r, awq(), awq(), act=5) == moeq.EDTYPE
     assert swiglu(L, r, awq(), awq(), fn=(-1.0, 1.0, 0.0)) == moeq.EINVAL
     assert swiglu(L, r, awq(), awq(), fn=(7.0, 1.702, 1.0, 1)) == moeq.OK   # one-sided gate
@@ -182,7 +182,8 @@ def test_down_and_backward_validation(L):
     assert b(None, 0, awq(E=1)) == moeq.OK           # single frozen projection
     assert b(None, 4, awq(E=2)) == moeq.ERANGE
     assert b(None, 4, bank(E=1, inter=0)) == moeq.EUNSUPPORTED
-    assert b(None, 4, awq(E=1), gdt=moeq.F16) == moeq.EUNSUPPORTED
+    assert b(None, 0, awq(E=1), gdt=moeq.F16) == moeq.OK
+    assert b(None, 4, awq(E=1), gdt=7) == moeq.EDTYPE
     assert b(None, -1, awq(E=1)) == moeq.EINVAL
 
 
@@ -258,7 +259,8 @@ def test_backward_path_validation(L):
     assert sib(r, up=awq(K=64, N=32, sdt=moeq.F16)) == moeq.EDTYPE
     assert sib(r, gate=awq(K=64, N=32, bias=FAKE)) == moeq.EINVAL
     assert sib(r, down=bank(K=32, R=64, inter=0)) == moeq.EUNSUPPORTED
-    assert sib(r, act=moeq.F16) == moeq.EUNSUPPORTED
+    assert sib(r0, act=moeq.F16) == moeq.OK              # fp16 rows: VALU kernels
+    assert sib(r, act=6) == moeq.EDTYPE
     assert sib(r, fn=(-2.0, 1.0, 0.0)) == moeq.EINVAL
     assert sib(r, down=awq(E=4, K=32, N=64)) == moeq.ERANGE
 
@@ -283,7 +285,8 @@ def test_unsorted_and_single_projection_validation(L):
     assert fwd(rows=0) == moeq.OK
     assert fwd(rows=-1) == moeq.EINVAL
     assert fwd(act=4) == moeq.EDTYPE
-    assert fwd(act=moeq.F16) == moeq.EUNSUPPORTED
+    assert fwd(rows=0, act=moeq.F16) == moeq.OK        # fp16 rows pass the dtype check
+    assert fwd(act=moeq.F16, y=0) == moeq.EINVAL
     assert fwd(w=awq(E=8, K=64, N=36)) == moeq.ESHAPE
     assert fwd(w=awq(E=4096, K=64, N=32)) == moeq.EUNSUPPORTED
     assert fwd(y=0) == moeq.EINVAL
@@ -299,7 +302,8 @@ def test_unsorted_and_single_projection_validation(L):
         return L.awq_expert_input_backward(P, gdt, rows, P, C.byref(w), P,
                                            C.c_void_p(wsp) if wsp else None, nbytes, None)
     assert bwd(rows=0) == moeq.OK
-    assert bwd(gdt=moeq.F16) == moeq.EUNSUPPORTED
+    assert bwd(rows=0, gdt=moeq.F16) == moeq.OK
+    assert bwd(gdt=moeq.F16, wsp=0) == moeq.EINVAL
     assert bwd(w=bank(E=8, K=64, R=32, inter=0)) == moeq.EUNSUPPORTED
     assert bwd(wsp=0) == moeq.EINVAL
     assert bwd(nbytes=16) == moeq.EWORKSPACE
@@ -314,7 +318,8 @@ def test_unsorted_and_single_projection_validation(L):
                                     C.c_void_p(wsp) if wsp else None, nbytes, None)
     assert single(rows=0) == moeq.OK
     assert single(w=awq(E=2, K=64, N=32)) == moeq.ERANGE
-    assert single(act=moeq.F16) == moeq.EUNSUPPORTED
+    assert single(rows=0, act=moeq.F16) == moeq.OK
+    assert single(act=moeq.F16, x=0) == moeq.EINVAL
     assert single(x=0) == moeq.EINVAL
     assert single(wsp=0) == moeq.EINVAL
     assert single(nbytes=need1 - 1) == moeq.EWORKSPACE
