@@ -73,12 +73,16 @@ struct WaveArgs {
     float gate_lo;  // lower clamp bound of the gate
     const __bf16 *dh;  // backward epilogue: [A, Nout] derivative of h (NULL: forward)
     __bf16 *out2;      // backward epilogue: dU (out holds dG)
+    int vec_out;       // 1: out 16-byte aligned and Nout % 8 == 0 (one-cube 16-byte stores)
 };
 
+// After the main loop: gate/up -- every wave's storage-rounded tile (G or U),
+// [wave][slot, row tile][lane] (the backward epilogue: the up waves' U tiles);
+// one cube -- the halves of the plane waves' tiles that they swap.
 template <int NSETS>
 struct WaveLds {
-    __bf16 A[2][kWaveRows][32];                              // A tile, double-buffered
-    uint2 U[NSETS == 2 ? kWaves / 2 : 1][4 * kRT][64];       // U tiles of the up waves
+    __bf16 A[2][kWaveRows][32];                                 // A tile, double-buffered
+    uint2 U[NSETS == 2 ? kWaves : kWaves / 2][4 * kRT][64];
 };
 
 template <int NSETS, int SD, int SPG, int DEPTH, bool BWD>
@@ -156,11 +160,6 @@ void awq_wave_kernel(WaveArgs a) {
         // step s: A fragments from lds.A[s & 1]; words from ring slot d = s % DEPTH
         auto step = [&](int s, int d) {
             const int buf = s & 1;
-            bf16x8 af[RT];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                af[rt] = *reinterpret_cast<const bf16x8 *>(
-                    &lds.A[buf][rt * 16 + c][8 * (grp ^ ((c >> 1) & 3))]);
             uint32_t pl[8];  // this wave's nibble plane of the eight words
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -170,6 +169,12 @@ void awq_wave_kernel(WaveArgs a) {
             const int dn = (d + 1) % DEPTH;
             store_rows(dn, buf ^ 1);
             issue_rows(dn, 32 * (s + 1 + DEPTH));
+            // the four B operands of the step first, then the row tiles one by
+            // one, each A fragment read from LDS just before its four MFMAs: a
+            // few fragments live at a time instead of eight keeps the kernel
+            // within two waves' registers (no spill, so no wait on the whole
+            // load ring for a spill reload)
+            bf16x8 bop[4];
 #pragma unroll
             for (int pr = 0; pr < 2; ++pr) {
                 f32x2 qv[8];
@@ -185,12 +190,17 @@ void awq_wave_kernel(WaveArgs a) {
                     for (int p = 0; p < 4; ++p)
                         op[p] = pack_bf16(coeff<SD>(qv[2 * p][h], gc, s4),
                                           coeff<SD>(qv[2 * p + 1][h], gc, s4));
-                    const bf16x8 bop = __builtin_bit_cast(bf16x8, op);
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt)
-                        acc[s4][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt], bop,
-                                                                              acc[s4][rt], 0, 0, 0);
+                    bop[s4] = __builtin_bit_cast(bf16x8, op);
                 }
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const bf16x8 af = *reinterpret_cast<const bf16x8 *>(
+                    &lds.A[buf][rt * 16 + c][8 * (grp ^ ((c >> 1) & 3))]);
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+                    acc[s4][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bop[s4],
+                                                                          acc[s4][rt], 0, 0, 0);
             }
             lds_barrier();
         };
@@ -241,6 +251,57 @@ void awq_wave_kernel(WaveArgs a) {
         bias_v[s4] = (active && a.bias[set]) ? load_f<SD>(a.bias[set], (size_t)e * N + col) : 0.0f;
     }
     const int rtn = (m1 - m0 + 15) >> 4;  // row tiles holding rows
+    if constexpr (NSETS == 2 && !BWD) {
+        if (a.vec_out) {
+            // Every wave leaves its tile, bias added and rounded to storage (G or
+            // U), in LDS.  Wave (column group, plane p, set s) then finishes row
+            // tiles 2(2p + s) and 2(2p + s) + 1 for all eight columns of its
+            // lanes' word columns, and stores each row's eight as one 16 bytes.
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const f32x4 v = acc[s4][rt];
+                    const float b = bias_v[s4];
+                    lds.U[wv][s4 * RT + rt][lane] =
+                        uint2{pack_bf16(v[0] + b, v[1] + b), pack_bf16(v[2] + b, v[3] + b)};
+                }
+            __syncthreads();
+            if (!active) return;
+            const int w0 = wv & ~3;  // wave (column group, plane 0, gate)
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2) {
+                const int rt = 2 * (wv & 3) + r2;
+                if (rt >= rtn) continue;
+                float h[8][4];  // [column of the word column][row i]
+#pragma unroll
+                for (int col = 0; col < 8; ++col) {
+                    // column col sits in slot sl = 2 (col & 3) + (col >> 2) of the
+                    // words: nibble plane sl >> 2, plane slot sl & 3
+                    const int sl = 2 * (col & 3) + (col >> 2);
+                    const int pw = w0 + 2 * (sl >> 2), s4 = sl & 3;
+                    const uint2 gg = lds.U[pw][s4 * RT + rt][lane];
+                    const uint2 uu = lds.U[pw + 1][s4 * RT + rt][lane];
+                    const float gv[4] = {__uint_as_float(gg.x << 16), __uint_as_float(gg.x & 0xFFFF0000u),
+                                         __uint_as_float(gg.y << 16), __uint_as_float(gg.y & 0xFFFF0000u)};
+                    const float uv[4] = {__uint_as_float(uu.x << 16), __uint_as_float(uu.x & 0xFFFF0000u),
+                                         __uint_as_float(uu.y << 16), __uint_as_float(uu.y & 0xFFFF0000u)};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        h[col][i] = swiglu_f(gv[i], uv[i], a.clamp, a.gate_lo, a.alpha, a.up_offset);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = m0 + rt * 16 + grp * 4 + i;
+                    if (row >= m1) continue;
+                    const u32x4 pk{pack_bf16(h[0][i], h[1][i]), pack_bf16(h[2][i], h[3][i]),
+                                   pack_bf16(h[4][i], h[5][i]), pack_bf16(h[6][i], h[7][i])};
+                    *reinterpret_cast<u32x4 *>(a.out + (size_t)row * a.Nout + 8 * j) = pk;
+                }
+            }
+            return;
+        }
+    }
     if constexpr (NSETS == 2) {
         const int pair = wv >> 1;  // (column group, plane)
         // backward: the gate waves fetch their dh pairs before the U hand-off
@@ -341,6 +402,47 @@ void awq_wave_kernel(WaveArgs a) {
                 o[2] = pack_bf16(hv[i][1], hv[i][3]);
             }
         }
+    } else if (a.vec_out) {
+        // The two plane waves of a column group hold columns {0,1,4,5} and
+        // {2,3,6,7} of each word column's eight.  Each sends the other the
+        // rows of half its row tiles (plane 0 keeps tiles 0-3, plane 1 tiles
+        // 4-7) through LDS, then stores whole 16-byte chunks of its rows.
+        const int pr = wv >> 1;  // column group within the block
+        auto pack_row = [&](int rt_, int i) {  // {cols 2p,2p+1 ; cols 4+2p,5+2p}
+            float v[4];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) v[s4] = acc[s4][rt_][i] + bias_v[s4];
+            return uint2{pack_bf16(v[0], v[2]), pack_bf16(v[1], v[3])};
+        };
+        auto swap_store = [&](auto plane_tag) {
+            constexpr int PL = decltype(plane_tag)::value;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lds.U[pr][PL * 16 + r4 * 4 + i][lane] = pack_row(PL ? r4 : 4 + r4, i);
+            __syncthreads();
+            if (!active) return;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int rt = PL ? 4 + r4 : r4;
+                if (rt >= rtn) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = m0 + rt * 16 + grp * 4 + i;
+                    if (row >= m1) continue;
+                    const uint2 own = pack_row(rt, i);
+                    const uint2 oth = lds.U[pr][(1 - PL) * 16 + r4 * 4 + i][lane];
+                    const u32x4 pk = PL ? u32x4{oth.x, own.x, oth.y, own.y}
+                                        : u32x4{own.x, oth.x, own.y, oth.y};
+                    *reinterpret_cast<u32x4 *>(a.out + (size_t)row * a.Nout + 8 * j) = pk;
+                }
+            }
+        };
+        if (plane)
+            swap_store(std::integral_constant<int, 1>{});
+        else
+            swap_store(std::integral_constant<int, 0>{});
     } else {
         if (!active) return;
 #pragma unroll
@@ -391,6 +493,7 @@ hipError_t run_wave(const ProjProblem &p, hipStream_t s) {
     a.up_offset = p.up_offset;
     a.dh = static_cast<const __bf16 *>(p.in2);
     a.out2 = static_cast<__bf16 *>(p.out2);
+    a.vec_out = ((uintptr_t)p.out % 16) == 0 && p.Nout % 8 == 0;
     // m-tiles are at most ceil(A / 128) + E; blocks past the last tile exit
     const long mtiles = ((long)p.rows + kWaveRows - 1) / kWaveRows + p.E;
     const long blocks = 8 * ((mtiles + 7) / 8) * a.nblk;
