@@ -66,6 +66,7 @@ struct MxArgs {
     int nblk;  // blocks per m-tile
     float clamp, alpha, up_offset;
     float gate_lo;  // lower clamp bound of the gate
+    int vec_out;    // 1: out 16-byte aligned and Nout % 8 == 0 (staged 16-byte stores)
 };
 
 __device__ __forceinline__ float e8m0_scale(uint32_t b) {
@@ -252,6 +253,70 @@ void mx_wave_kernel(MxArgs a) {
     // ---- epilogue.  Lane (c, grp) holds, for column tile ct and row tile rt,
     // rows 16 rt + 4 grp + i of bank row n0 + 16 ct + c.
     const __bf16 *bias = a.bias + (size_t)e * R;
+    if (a.vec_out) {
+        // The block's outputs go through LDS (the A tiles are free now) and
+        // leave as whole 16-byte chunks of each row: a block row is 192 h
+        // features (gate/up) or 384 outputs, contiguous in out.  gate/up takes
+        // one pass over the 128 rows, one bank two passes of 64 rows.
+        constexpr bool SW = MODE == PROJ_BANK_SWIGLU;
+        constexpr int COLS = SW ? kWaves * kCT * 8 : kWaves * kCT * 16;
+        constexpr int PROWS = SW ? kRows : kRows / 2;
+        constexpr int CH = COLS / 8;  // 16-byte chunks per staged row
+        static_assert(PROWS * COLS <= 2 * kRows * kArow, "staging fits in the A tiles");
+        __bf16 *st = &As[0][0][0];
+        const int col0 = nb * kWaves * kCT * (SW ? 8 : 16);  // first output column of the block
+        const int wcol = wv * kCT * 16;                     // first bank row of the wave, block-local
+        __syncthreads();  // every wave is done with the A tiles
+#pragma unroll
+        for (int pass = 0; pass < kRows / PROWS; ++pass) {
+#pragma unroll
+            for (int ct = 0; ct < kCT; ++ct) {
+                const int r = n0 + ct * 16 + c;
+                const float b = r < R ? (float)bias[r] : 0.0f;
+#pragma unroll
+                for (int rt = pass * (PROWS / 16); rt < (pass + 1) * (PROWS / 16); ++rt) {
+                    if (rt >= rtn) continue;
+                    const int rl = rt * 16 + grp * 4 - pass * PROWS;  // staged row of i = 0
+                    if constexpr (SW) {
+                        const bool gate_lane = (c & 1) == 0;
+                        float own[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) own[i] = round_to<MOEQ_BF16>(acc[ct][rt][i] + b);
+                        const float s0 = gate_lane ? own[2] : own[0];
+                        const float s1 = gate_lane ? own[3] : own[1];
+                        const float p0 = __int_as_float(
+                            __builtin_amdgcn_mov_dpp(__float_as_int(s0), 0xB1, 0xF, 0xF, false));
+                        const float p1 = __int_as_float(
+                            __builtin_amdgcn_mov_dpp(__float_as_int(s1), 0xB1, 0xF, 0xF, false));
+                        const int f = (wcol + ct * 16 + c) >> 1;  // block-local feature
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const float mine = gate_lane ? own[q] : own[2 + q];
+                            const float other = q == 0 ? p0 : p1;
+                            const float gv = gate_lane ? mine : other;
+                            const float uv = gate_lane ? other : mine;
+                            st[(rl + (gate_lane ? q : 2 + q)) * COLS + f] =
+                                (__bf16)swiglu_f(gv, uv, a.clamp, a.gate_lo, a.alpha, a.up_offset);
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            st[(rl + i) * COLS + wcol + ct * 16 + c] = (__bf16)(acc[ct][rt][i] + b);
+                    }
+                }
+            }
+            __syncthreads();
+            for (int u = threadIdx.x; u < PROWS * CH; u += kThreads) {
+                const int rl = u / CH, ch = u - rl * CH;
+                const int row = m0 + pass * PROWS + rl, col = col0 + 8 * ch;
+                if (row < m1 && col < a.Nout)
+                    *reinterpret_cast<u32x4 *>(a.out + (size_t)row * a.Nout + col) =
+                        *reinterpret_cast<const u32x4 *>(st + rl * COLS + 8 * ch);
+            }
+            if (pass + 1 < kRows / PROWS) __syncthreads();
+        }
+        return;
+    }
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) {
         const int r = n0 + ct * 16 + c;
@@ -333,6 +398,7 @@ hipError_t launch_mx(const ProjProblem &p, hipStream_t s) {
     a.gate_lo = p.gate_lo;
     a.alpha = p.alpha;
     a.up_offset = p.up_offset;
+    a.vec_out = ((uintptr_t)p.out % 16) == 0 && p.Nout % 8 == 0;
     const int rows_per_block = kWaves * kCT * 16;
     a.nblk = (a.R + rows_per_block - 1) / rows_per_block;
     const long mtiles = ((long)p.rows + kRows - 1) / kRows + p.E;

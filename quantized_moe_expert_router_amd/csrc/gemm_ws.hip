@@ -78,6 +78,7 @@ struct WsArgs {
     float gate_lo;  // lower clamp bound of the gate
     const __bf16 *dh;  // backward epilogue: [A, Nout] derivative of h (NULL: forward)
     __bf16 *out2;      // backward epilogue: dU (out holds dG)
+    int vec_out;       // 1: out 16-byte aligned and Nout % 8 == 0 (staged 16-byte stores)
 };
 
 __device__ __forceinline__ int lds_chunk(int row, int ch) { return ch ^ ((row >> 1) & 3); }
@@ -233,11 +234,11 @@ void awq_ws_kernel(WsArgs a) {
             produce(q, I2{});
             lds_barrier();
         }
-        return;
     }
 
     // ======================================================= consumer waves
-    const int wm = wv >> 2, wn = wv & 3;  // 64-row half, column quarter
+    // (the producer waves pass through to the epilogue's barriers)
+    const int wm = (wv >> 2) & 1, wn = wv & 3;  // 64-row half, column quarter
     // column tiles: gate/up -- tile t < 4 gate, t + 4 the up tile of the same
     // logical columns (slot 2 wn + (t >> 1), word columns (t & 1) * 16 + c);
     // one cube -- slot 2 wn + (t >> 2), word columns (t & 3) * 16 + c
@@ -284,7 +285,7 @@ void awq_ws_kernel(WsArgs a) {
             lds_barrier();
         }
     };
-    switch (rtn) {
+    if (wv < kCons) switch (rtn) {
     case 4: consume(std::integral_constant<int, 4>{}); break;
     case 3: consume(std::integral_constant<int, 3>{}); break;
     case 2: consume(std::integral_constant<int, 2>{}); break;
@@ -295,6 +296,70 @@ void awq_ws_kernel(WsArgs a) {
     // ---- epilogue: lane (c, grp) holds, for row tile rt and column tile t,
     // rows rbase + 16 rt + 4 grp + i of the logical column of tile t, lane c
     const int jb = nb * (NSETS == 2 ? kWc / 2 : kWc);  // first word column of the block
+    if (a.vec_out && !(NSETS == 2 && a.dh)) {
+        // The block's outputs go through LDS (the B tiles are free now) and
+        // all twelve waves store whole 16-byte chunks of each row: a block row
+        // is 256 h columns (gate/up) or 512 outputs, contiguous in out.
+        // gate/up takes one pass over the 128 rows, one cube a pass per
+        // 64-row half.
+        constexpr int COLS = NSETS == 2 ? kWc * 4 : kWc * 8;
+        constexpr int PROWS = NSETS == 2 ? kRows : kRows / 2;
+        constexpr int CH = COLS / 8;
+        static_assert(PROWS * COLS <= 2 * kBCols * 32, "staging fits in the B tiles");
+        __bf16 *st = &Bs[0][0][0];
+        __syncthreads();  // every wave is done with the tiles
+#pragma unroll
+        for (int pass = 0; pass < kRows / PROWS; ++pass) {
+            if (wv < kCons && (NSETS == 2 || wm == pass)) {
+#pragma unroll
+                for (int t = 0; t < (NSETS == 2 ? 4 : 8); ++t) {
+                    const int col = tcol(t);
+                    int sl, wcol;
+                    if (NSETS == 2) {
+                        sl = (col & 255) >> 5;
+                        wcol = (col & 31) + c;
+                    } else {
+                        sl = col >> 6;
+                        wcol = (col & 63) + c;
+                    }
+                    const int n = 8 * wcol + kSlotCol[sl];  // block-local output column
+                    const bool on = jb + wcol < W;
+                    const size_t nb_ = (size_t)e * N + 8 * jb + n;
+                    const float b0 = (on && a.bias[0]) ? load_f<SD>(a.bias[0], nb_) : 0.0f;
+                    const float b1 = (NSETS == 2 && on && a.bias[1]) ? load_f<SD>(a.bias[1], nb_)
+                                                                     : 0.0f;
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) {
+                        if (rt >= rtn) continue;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int rl = (NSETS == 2 ? wm * 64 : 0) + rt * 16 + grp * 4 + i;
+                            float v;
+                            if (NSETS == 2) {
+                                const float gv = round_to<MOEQ_BF16>(acc[rt][t][i] + b0);
+                                const float uv = round_to<MOEQ_BF16>(acc[rt][t + 4][i] + b1);
+                                v = swiglu_f(gv, uv, a.clamp, a.gate_lo, a.alpha, a.up_offset);
+                            } else {
+                                v = acc[rt][t][i] + b0;
+                            }
+                            st[rl * COLS + n] = (__bf16)v;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            for (int u = threadIdx.x; u < PROWS * CH; u += kThreads) {
+                const int rl = u / CH, ch = u - rl * CH;
+                const int row = m0 + pass * PROWS + rl, col = 8 * jb + 8 * ch;
+                if (row < m1 && col < a.Nout)
+                    *reinterpret_cast<u32x4 *>(a.out + (size_t)row * a.Nout + col) =
+                        *reinterpret_cast<const u32x4 *>(st + rl * COLS + 8 * ch);
+            }
+            if (pass + 1 < kRows / PROWS) __syncthreads();
+        }
+        return;
+    }
+    if (wv >= kCons) return;
 #pragma unroll
     for (int t = 0; t < (NSETS == 2 ? 4 : 8); ++t) {
         const int col = tcol(t);
@@ -370,6 +435,7 @@ hipError_t run_ws(const ProjProblem &p, hipStream_t s) {
     a.up_offset = p.up_offset;
     a.dh = static_cast<const __bf16 *>(p.in2);
     a.out2 = static_cast<__bf16 *>(p.out2);
+    a.vec_out = ((uintptr_t)p.out % 16) == 0 && p.Nout % 8 == 0;
     const long mtiles = ((long)p.rows + kRows - 1) / kRows + p.E;
     const long blocks = 8 * ((mtiles + 7) / 8) * a.nblk;
     hipLaunchKernelGGL((awq_ws_kernel<NSETS, SD>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
