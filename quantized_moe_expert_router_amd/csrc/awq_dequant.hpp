@@ -47,14 +47,16 @@ __device__ __forceinline__ void decode_codes(uint32_t w, float q[8]) {
 template <int SD>
 struct GroupConst {
     float s[8];   // scale * 2^9
-    float zs[8];  // -zero * scale (16-bit scales) | zero * 2^-9 (fp32 scales)
+    float zs[8];  // -zero * scale (rounded to fp32 for fp32 scales)
 };
 
 // Coefficient of slot sl from q = code * 2^-9, as the scale-dtype value in fp32.
+// 16-bit scales: the fma is the exact (code - zero) * scale.  fp32 scales: the
+// MFMA operand is bf16 anyway, so the one-op code * scale - RN(zero * scale)
+// (within one fp32 ulp of RNE32((code - zero) * scale)) goes to the bf16 pack.
 template <int SD>
 __device__ __forceinline__ float coeff(float q, const GroupConst<SD> &gc, int sl) {
-    if (SD == MOEQ_F32) return (q - gc.zs[sl]) * gc.s[sl];        // RNE32((code-zero)s)
-    const float v = __builtin_fmaf(q, gc.s[sl], gc.zs[sl]);         // exact (code-zero)s
+    const float v = __builtin_fmaf(q, gc.s[sl], gc.zs[sl]);
     return SD == MOEQ_F16 ? (float)(_Float16)v : v;                 // bf16: rounded at pack
 }
 
@@ -156,7 +158,7 @@ __device__ __forceinline__ void decode_group(const GroupRaw<SD> &r, GroupConst<S
     for (int sl = 0; sl < 8; ++sl) {
         const float sc = sv[kSlotCol[sl]];
         gc.s[sl] = sc * kCodeUnit;                                          // exact
-        gc.zs[sl] = SD == MOEQ_F32 ? z[sl] : -(z[sl] * kCodeUnit) * sc;    // exact: 4 x 16 bits
+        gc.zs[sl] = -(z[sl] * kCodeUnit) * sc;  // 16-bit scales: exact (4 x 16 bits)
     }
 }
 

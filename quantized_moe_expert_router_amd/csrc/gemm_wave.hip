@@ -529,7 +529,7 @@ bool wave_fits(const ProjProblem &p) {
     if (p.act != MOEQ_BF16 || p.w0.format != MOEQ_FMT_AWQ || !p.offsets || !p.tile_offsets)
         return false;
     if (p.w0.g != 64 && p.w0.g != 128) return false;
-    if (p.w0.sdt == MOEQ_F32) return false;  // two-op coefficients: the LDS-tiled kernel is faster
+    if (p.w0.sdt == MOEQ_F32) return false;  // fp32 scales: the warp-specialised kernel is faster
     if (p.w0.K % p.w0.g != 0) return false;
     if ((size_t)p.rows * p.w0.K * 2 >= ((size_t)1 << 31)) return false;  // 32-bit row offsets
     if (p.mode != PROJ_SWIGLU && p.mode != PROJ_PLAIN) return false;
