@@ -178,6 +178,44 @@ def test_stream_epilogue_unaligned_outputs():
     assert torch.equal(y_al, y_un)
 
 
+def _unaligned(rows, cols):
+    """A [rows, cols] bf16 view at a 2-byte offset from a 16-byte aligned block."""
+    t = torch.empty(rows * cols + 1, dtype=torch.bfloat16, device=DEV)[1:].view(rows, cols)
+    assert t.data_ptr() % 16 != 0
+    return t
+
+
+@pytest.mark.parametrize("kernel,fmt,sdt,T,E,k,H,I", [
+    ("wave", "awq", "bf16", 333, 3, 2, 512, 384),   # ragged m-tiles, 3 column groups of gate/up
+    ("ws", "awq", "f32", 333, 3, 2, 512, 384),
+    ("mx", "mxfp4", "bf16", 150, 6, 3, 288, 160),   # partial column tiles, 2-8 live row tiles
+])
+def test_mfma_epilogue_unaligned_outputs(kernel, fmt, sdt, T, E, k, H, I, monkeypatch):
+    """The m-tile kernels store whole 16-byte row chunks (staged through LDS) when
+    the output is 16-byte aligned and fall back to per-lane stores otherwise; both
+    must give the same h and y bit for bit, for gate/up (SwiGLU) and down."""
+    if kernel == "ws":
+        monkeypatch.setenv("MOEQ_WAVE", "0")
+    base = CONFIGS["mxfp4" if fmt == "mxfp4" else "prefill"]
+    cfg = dataclasses.replace(base, T=T, E=E, k=k, H=H, I=I, sdt=sdt,
+                              awq_bias=fmt == "awq" and sdt == "f32")
+    p = make_inputs(cfg, seed=3 * T + E)
+    print(f"[epilogue {kernel}] T={T} E={E} k={k} H={H} I={I} sdt={sdt}", flush=True)
+    d = di.upload(p, DEV)
+    disp = moeq.moe_dispatch(d["x"], d["logits"], d["router_bias"], p["k"])
+    r, A = disp["route"], T * k
+    args = (p["clamp"], p["alpha"], p["up_offset"])
+    h_al = moeq.awq_grouped_swiglu(r, disp["values"], d["gate"], d["up_arg"], *args)
+    h_un = _unaligned(A, I)
+    moeq.awq_grouped_swiglu(r, disp["values"], d["gate"], d["up_arg"], *args, h=h_un)
+    y_al = moeq.awq_grouped_down(r, h_al, d["down"])
+    y_un = _unaligned(A, H)
+    moeq.awq_grouped_down(r, h_al, d["down"], y=y_un)
+    torch.cuda.synchronize()
+    assert torch.equal(h_al, h_un)
+    assert torch.equal(y_al, y_un)
+
+
 @pytest.mark.parametrize("T,E,k", [
     (50, 200, 6),      # fused small dispatch, 16 keys per lane (unsorted rounds)
     (256, 256, 16),    # the fused kernel's largest shape: T = 256, A = 4096, E = 256, k = 16
