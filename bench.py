@@ -430,7 +430,10 @@ def median_step(torch, steps, R, graphs):
 def call_ms(torch, launch, R, launches):
     """Per-launch time of one call: a graph of `launches` back-to-back launches
     (replica i % R for launch i), replayed and timed with events on the stream
-    it is replayed on, divided by the launch count."""
+    it is replayed on, divided by the launch count.  Three untimed replays
+    first, then the median of three timed rounds of five replays: the first
+    replays after the other calls' timing run slower (the GFX clock settles),
+    and a single round caught that transient."""
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -442,17 +445,20 @@ def call_ms(torch, launch, R, launches):
     with torch.cuda.graph(g):
         for i in range(launches):
             launch(i)
-    g.replay()
+    for _ in range(3):
+        g.replay()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    reps = 5
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(reps):
-        g.replay()
-    b.record(stream)
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / (reps * launches)
+    reps, rounds = 5, []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        rounds.append(a.elapsed_time(b) / (reps * launches))
+    return sorted(rounds)[1]
 
 
 def measure_forward(cfg, args, steps, warmup, mx8=False):
