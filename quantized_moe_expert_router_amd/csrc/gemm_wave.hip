@@ -251,12 +251,13 @@ void awq_wave_kernel(WaveArgs a) {
         bias_v[s4] = (active && a.bias[set]) ? load_f<SD>(a.bias[set], (size_t)e * N + col) : 0.0f;
     }
     const int rtn = (m1 - m0 + 15) >> 4;  // row tiles holding rows
-    if constexpr (NSETS == 2 && !BWD) {
+    if constexpr (NSETS == 2) {
         if (a.vec_out) {
             // Every wave leaves its tile, bias added and rounded to storage (G or
             // U), in LDS.  Wave (column group, plane p, set s) then finishes row
             // tiles 2(2p + s) and 2(2p + s) + 1 for all eight columns of its
-            // lanes' word columns, and stores each row's eight as one 16 bytes.
+            // lanes' word columns, and stores each row's eight as one 16 bytes
+            // (backward: reads dh and stores dG and dU the same way).
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -273,7 +274,7 @@ void awq_wave_kernel(WaveArgs a) {
             for (int r2 = 0; r2 < 2; ++r2) {
                 const int rt = 2 * (wv & 3) + r2;
                 if (rt >= rtn) continue;
-                float h[8][4];  // [column of the word column][row i]
+                float gq[8][4], uq[8][4];  // [column of the word column][row i]
 #pragma unroll
                 for (int col = 0; col < 8; ++col) {
                     // column col sits in slot sl = 2 (col & 3) + (col >> 2) of the
@@ -282,21 +283,47 @@ void awq_wave_kernel(WaveArgs a) {
                     const int pw = w0 + 2 * (sl >> 2), s4 = sl & 3;
                     const uint2 gg = lds.U[pw][s4 * RT + rt][lane];
                     const uint2 uu = lds.U[pw + 1][s4 * RT + rt][lane];
-                    const float gv[4] = {__uint_as_float(gg.x << 16), __uint_as_float(gg.x & 0xFFFF0000u),
-                                         __uint_as_float(gg.y << 16), __uint_as_float(gg.y & 0xFFFF0000u)};
-                    const float uv[4] = {__uint_as_float(uu.x << 16), __uint_as_float(uu.x & 0xFFFF0000u),
-                                         __uint_as_float(uu.y << 16), __uint_as_float(uu.y & 0xFFFF0000u)};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        h[col][i] = swiglu_f(gv[i], uv[i], a.clamp, a.gate_lo, a.alpha, a.up_offset);
+                    gq[col][0] = __uint_as_float(gg.x << 16);
+                    gq[col][1] = __uint_as_float(gg.x & 0xFFFF0000u);
+                    gq[col][2] = __uint_as_float(gg.y << 16);
+                    gq[col][3] = __uint_as_float(gg.y & 0xFFFF0000u);
+                    uq[col][0] = __uint_as_float(uu.x << 16);
+                    uq[col][1] = __uint_as_float(uu.x & 0xFFFF0000u);
+                    uq[col][2] = __uint_as_float(uu.y << 16);
+                    uq[col][3] = __uint_as_float(uu.y & 0xFFFF0000u);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = m0 + rt * 16 + grp * 4 + i;
                     if (row >= m1) continue;
-                    const u32x4 pk{pack_bf16(h[0][i], h[1][i]), pack_bf16(h[2][i], h[3][i]),
-                                   pack_bf16(h[4][i], h[5][i]), pack_bf16(h[6][i], h[7][i])};
-                    *reinterpret_cast<u32x4 *>(a.out + (size_t)row * a.Nout + 8 * j) = pk;
+                    const size_t at = (size_t)row * a.Nout + 8 * j;
+                    if constexpr (BWD) {
+                        const u32x4 dw = *reinterpret_cast<const u32x4 *>(a.dh + at);
+                        float dg[8], du[8];
+#pragma unroll
+                        for (int col = 0; col < 8; ++col) {
+                            const uint32_t pr2 = dw[col >> 1];
+                            const float dv = __uint_as_float((col & 1) ? (pr2 & 0xFFFF0000u)
+                                                                       : (pr2 << 16));
+                            swiglu_vjp_f(gq[col][i], uq[col][i], dv, a.clamp, a.gate_lo, a.alpha,
+                                         a.up_offset, &dg[col], &du[col]);
+                        }
+                        *reinterpret_cast<u32x4 *>(a.out + at) =
+                            u32x4{pack_bf16(dg[0], dg[1]), pack_bf16(dg[2], dg[3]),
+                                  pack_bf16(dg[4], dg[5]), pack_bf16(dg[6], dg[7])};
+                        *reinterpret_cast<u32x4 *>(a.out2 + at) =
+                            u32x4{pack_bf16(du[0], du[1]), pack_bf16(du[2], du[3]),
+                                  pack_bf16(du[4], du[5]), pack_bf16(du[6], du[7])};
+                    } else {
+                        float h[8];
+#pragma unroll
+                        for (int col = 0; col < 8; ++col)
+                            h[col] = swiglu_f(gq[col][i], uq[col][i], a.clamp, a.gate_lo, a.alpha,
+                                              a.up_offset);
+                        *reinterpret_cast<u32x4 *>(a.out + at) =
+                            u32x4{pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]),
+                                  pack_bf16(h[4], h[5]), pack_bf16(h[6], h[7])};
+                    }
                 }
             }
             return;
@@ -493,7 +520,8 @@ hipError_t run_wave(const ProjProblem &p, hipStream_t s) {
     a.up_offset = p.up_offset;
     a.dh = static_cast<const __bf16 *>(p.in2);
     a.out2 = static_cast<__bf16 *>(p.out2);
-    a.vec_out = ((uintptr_t)p.out % 16) == 0 && p.Nout % 8 == 0;
+    a.vec_out = (((uintptr_t)p.out | (uintptr_t)p.out2 | (uintptr_t)p.in2) % 16) == 0 &&
+                p.Nout % 8 == 0;
     // m-tiles are at most ceil(A / 128) + E; blocks past the last tile exit
     const long mtiles = ((long)p.rows + kWaveRows - 1) / kWaveRows + p.E;
     const long blocks = 8 * ((mtiles + 7) / 8) * a.nblk;
