@@ -244,6 +244,34 @@ def cpu_baseline(cfg, target_s):
                       f"({el:.1f} s, double accumulation, OpenMP)"}
 
 
+def cpu_single_core(target_s):
+    """Single-core figures of the oracle (one OpenMP thread) for the tiny
+    workload and a 4-token sample of the decode workload."""
+    import ctypes
+    import oracle
+    from quantized_moe_expert_router_amd.synth import CONFIGS, make_inputs
+    oracle._load()
+    gomp = ctypes.CDLL("libgomp.so.1")  # the oracle's OpenMP runtime, already loaded
+    prev = gomp.omp_get_max_threads()
+    gomp.omp_set_num_threads(1)
+    out = {}
+    try:
+        for name, T in (("tiny", 16), ("decode", 4)):
+            p = make_inputs(CONFIGS[name], T=T)
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                oracle.moe_forward(p, keep_intermediates=False)
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= target_s or reps >= 1000:
+                    break
+            out[name] = {"value": round(reps * T / el, 3), "unit": "tokens/s", "cores": 1,
+                         "sample": f"{reps} x full forward of a {T}-token batch ({el:.1f} s)"}
+    finally:
+        gomp.omp_set_num_threads(prev)
+    return out
+
+
 def cpu_baseline_backward(cfg, target_s):
     """The oracle's backward steps as they stand, on a bounded sample."""
     import numpy as np
@@ -867,7 +895,16 @@ def main():
     if peaks:
         res["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        cb = cpu_baseline(cfg, args.cpu_seconds)
+        cb["gpu_over_cpu"] = round(res["value"] / cb["value"], 1) if cb["value"] else None
+        if not args.single and not mx8 and cfg.name == "decode":
+            cb["single_core"] = cpu_single_core(min(args.cpu_seconds, 4.0))
+            for name, w in res.get("workloads", {}).items():
+                wb = cpu_baseline(CONFIGS[name], min(args.cpu_seconds, 5.0))
+                wb["gpu_over_cpu"] = (round(w["tokens_per_s"] / wb["value"], 1)
+                                      if wb["value"] else None)
+                w["cpu_baseline"] = wb
+        res["cpu_baseline"] = cb
     print(json.dumps(res), flush=True)
 
 
