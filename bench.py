@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="after the warm-up steps, untimed replays of the step graphs for at "
+                         "least this long, so the timed steps start at steady clocks")
     ap.add_argument("--config", default="decode",
                     choices=["tiny", "decode", "prefill", "many", "mxfp4"])
     ap.add_argument("--single", action="store_true",
@@ -390,9 +393,24 @@ class Workload:
         self.combine(i)
 
 
+SETTLE_MS = 200.0  # set from --settle-ms
+
+
+def settle(torch, replay):
+    """Untimed replays until SETTLE_MS of wall time has passed: with a few warm-up
+    steps only, the first steps after a phase of other work run 5-10% slower
+    (the GPU clocks ramp), and a timed region of 20 decode steps is under 2 ms."""
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < SETTLE_MS:
+        for _ in range(8):
+            replay()
+        torch.cuda.synchronize()
+
+
 def warm_and_capture(torch, step, R, warmup, eager):
     """Warm-up on a side stream, then one graph per replica and one graph of a
-    whole cycle of R steps (as consecutive MoE layers of a model would be)."""
+    whole cycle of R steps (as consecutive MoE layers of a model would be), then
+    untimed replays of the cycle for SETTLE_MS."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -401,6 +419,8 @@ def warm_and_capture(torch, step, R, warmup, eager):
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     if eager:
+        it = iter(range(1 << 30))
+        settle(torch, lambda: step(next(it)))
         return None, None
     graphs = []
     for r in range(R):
@@ -416,6 +436,7 @@ def warm_and_capture(torch, step, R, warmup, eager):
         graphs[i % R].replay()
     cycle.replay()
     torch.cuda.synchronize()
+    settle(torch, cycle.replay)
     return graphs, cycle
 
 
@@ -703,7 +724,7 @@ def run_backward(cfg, args):
     rl["traffic"] = None
     res = {
         "metric": METRIC_BWD, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_ms": SETTLE_MS,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if cfg.adt == "bf16" else "f32",
         "data": "synthetic",
@@ -817,7 +838,9 @@ def summarize_traffic(dirs, kernel_sub, title, alg_bytes_per_launch=None):
 
 
 def main():
+    global SETTLE_MS
     args = parse()
+    SETTLE_MS = max(0.0, args.settle_ms)
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, args.title, args.tail)
         return
@@ -868,7 +891,7 @@ def main():
     with_measured(r["roofline_down"], peaks)
     res = {
         "metric": METRIC_MX8 if mx8 else METRIC, "value": r["tokens_per_s"], "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_ms": SETTLE_MS, "ms_per_step": r["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "mxfp8xmxfp4" if mx8 else ("bf16" if cfg.adt == "bf16" else "f32"),
         "data": "synthetic",
