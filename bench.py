@@ -779,6 +779,26 @@ def summarize_stats(d, title, tail=0):
             last = [d for _, d in ev[-tail:]]
             if len(ev) >= tail:
                 print(f"{name[:100]:100s} {len(last):6d} {sum(last) / len(last) / 1e3:9.2f}")
+    if traces:
+        # each dispatch by the kernel that ran before it: after another kernel (as
+        # inside the forward step) or after itself (the per-call timing graphs'
+        # back-to-back launches)
+        seq = []
+        with open(traces[0]) as f:
+            for r in csv.DictReader(f):
+                seq.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+        seq.sort()
+        ctx = {}
+        for (_, _, prev), (s0, e0, name) in zip(seq, seq[1:]):
+            ctx.setdefault(name, ([], []))[prev == name].append((e0 - s0) / 1e3)
+        med = lambda v: sorted(v)[len(v) // 2] if v else float("nan")
+        print("\n# median duration by the preceding dispatch: another kernel (in the step) or "
+              "the same kernel (back to back)")
+        print(f"{'kernel':100s} {'n_step':>6s} {'step_us':>9s} {'n_b2b':>6s} {'b2b_us':>9s}")
+        for name, (other, same) in sorted(ctx.items(), key=lambda kv: -sum(kv[1][0] + kv[1][1])):
+            if len(other) + len(same) >= 16:
+                print(f"{name[:100]:100s} {len(other):6d} {med(other):9.2f} {len(same):6d} "
+                      f"{med(same):9.2f}")
 
 
 def _counter_per_dispatch(d, counter, kernel_sub):
